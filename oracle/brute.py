@@ -1,0 +1,68 @@
+"""Scalar brute force for paged-attention decode (test infrastructure only).
+
+Pure-Python loops, Python floats (IEEE double).  Deliberately written without
+the range arithmetic of ``paged_attention``: it walks every position of the
+context and tests visibility per position with the page's wording — gllm
+"feat(backend): sliding-window PagedAttention" (#116), summary: with window
+> 0 the token at position p attends to positions p-window+1 through p,
+window == 0 is unlimited causal — i.e. t is visible iff t <= p and, when a
+window is set, fewer than ``window`` positions separate t from p.  Only for
+tiny inputs.
+"""
+
+from __future__ import annotations
+
+import math
+
+
+def brute_decode(q, k_cache, v_cache, block_tables, seq_lens, query_lens,
+                 scale, window, num_kv_heads, block_size):
+    """Same contract and layouts as ``paged_attention.decode`` (nested
+    lists or arrays indexed element by element).  Returns nested lists
+    [T][H_q][D] of floats."""
+    B = len(seq_lens)
+    H_q = len(q[0]) if len(q) else 0
+    D = len(q[0][0]) if len(q) else 0
+    group = H_q // num_kv_heads
+    sigma = float(_to_f32(scale))
+    out = []
+    row = 0
+    for b in range(B):
+        L = int(seq_lens[b])
+        nq = int(query_lens[b])
+        for i in range(nq):
+            p = L - nq + i                     # this token's own position
+            out_row = []
+            for hq in range(H_q):
+                kvh = hq // group
+                logits = []
+                where = []
+                for t in range(L):
+                    if t > p:
+                        continue               # causal: nothing after p
+                    if window != 0 and p - t >= window:
+                        continue               # more than window-1 back
+                    phys = int(block_tables[b][t // block_size])
+                    off = t % block_size
+                    dot = 0.0
+                    for d in range(D):
+                        dot += float(q[row][hq][d]) * float(k_cache[phys][kvh][off][d])
+                    logits.append(sigma * dot)
+                    where.append((phys, off))
+                top = max(logits)
+                wts = [math.exp(x - top) for x in logits]
+                tot = math.fsum(wts)
+                vec = []
+                for d in range(D):
+                    acc = math.fsum(w * float(v_cache[phys][kvh][d][off])
+                                    for w, (phys, off) in zip(wts, where))
+                    vec.append(acc / tot)
+                out_row.append(vec)
+            out.append(out_row)
+            row += 1
+    return out
+
+
+def _to_f32(x):
+    import struct
+    return struct.unpack("f", struct.pack("f", float(x)))[0]

@@ -1,0 +1,218 @@
+"""Seeded synthetic inputs for paged-attention decode.
+
+This module only draws random numbers and lays them out; it holds none of the
+attention arithmetic, so both the HIP path's tests/bench and the CPU oracle
+can consume what it produces without sharing code.
+
+Layouts (the library's contract):
+    q, out        [T, H_q, D], T = sum(query_lens), packed in sequence order
+    k_cache       [num_blocks, H_kv, block_size, D]
+    v_cache       [num_blocks, H_kv, D, block_size]
+    block_tables  int32 [B, max_blocks_per_seq]
+    seq_lens      int32 [B]  (context length, query tokens included)
+    query_lens    int32 [B]
+
+Recipe (also in the design doc): lengths and block tables come from a CPU
+``torch.Generator`` seeded with the workload's seed; the pool holds
+ceil(1.25 x needed) blocks unless the workload fixes it, and a seeded random
+permutation of the pool is dealt out to the sequences in order.  Table
+entries past a sequence's last block point at an unused pool block.  Q, K and
+V are N(0, 1) drawn in float32 with a generator seeded from the same seed on
+the target device, then rounded to the workload dtype (round-to-nearest-
+even).  With ``poison=True`` every pool block no table uses, and every slot
+at or past seq_len in a sequence's last block, is filled with NaN, so any
+read of memory outside the context shows up in the output.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, replace
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str                 # "f32" or "bf16" (q, k, v and out share it)
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    query_len: int
+    windows: tuple
+    scale: float
+    seed: int
+    max_blocks_per_seq: int
+    max_seq_len: int           # host-known upper bound on seq_lens
+    seq_lens: tuple = ()       # fixed lengths, or ...
+    len_range: tuple = ()      # ... uniform integers in [lo, hi]
+    query_lens: tuple = ()     # per-sequence query lengths (default: query_len each)
+    pool: int = 0              # physical blocks; 0 = ceil(1.25 x needed)
+    description: str = ""
+
+
+WORKLOADS = {
+    "tiny_f32": Workload(
+        name="tiny_f32", dtype="f32", batch=2, num_q_heads=4, num_kv_heads=1,
+        head_dim=64, block_size=16, query_len=1, windows=(0, 5), scale=1.0 / 8.0,
+        seed=1, max_blocks_per_seq=4, max_seq_len=50, seq_lens=(37, 50), pool=16,
+        description="tiny fp32 paged decode: B=2, 4/1 heads, D=64, bs=16, "
+                    "pool 16, context 37 and 50, q_len 1, window 0 and 5"),
+    "gqa_bf16": Workload(
+        name="gqa_bf16", dtype="bf16", batch=32, num_q_heads=32, num_kv_heads=8,
+        head_dim=128, block_size=16, query_len=1, windows=(0,),
+        scale=1.0 / math.sqrt(128.0), seed=2, max_blocks_per_seq=512,
+        max_seq_len=8192, len_range=(512, 8192),
+        description="GQA decode bf16: B=32, 32/8 heads, D=128, bs=16, "
+                    "context U[512, 8192], q_len 1, window 0"),
+    "swa_mtp_bf16": Workload(
+        name="swa_mtp_bf16", dtype="bf16", batch=64, num_q_heads=64, num_kv_heads=8,
+        head_dim=64, block_size=64, query_len=4, windows=(128,), scale=1.0 / 8.0,
+        seed=3, max_blocks_per_seq=512, max_seq_len=32768, len_range=(1024, 32768),
+        description="sliding-window MTP decode bf16: B=64, 64/8 heads, D=64, "
+                    "bs=64, context U[1024, 32768], q_len 4, window 128"),
+    "long_splitk_bf16": Workload(
+        name="long_splitk_bf16", dtype="bf16", batch=1, num_q_heads=8, num_kv_heads=1,
+        head_dim=128, block_size=16, query_len=1, windows=(0,),
+        scale=1.0 / math.sqrt(128.0), seed=4, max_blocks_per_seq=8192,
+        max_seq_len=131072, seq_lens=(131072,), pool=10240,
+        description="single-KV-group long-context split-K decode bf16: B=1, "
+                    "8/1 heads, D=128, bs=16, context 131072, q_len 1, window 0"),
+    "large_block_mtp_bf16": Workload(
+        name="large_block_mtp_bf16", dtype="bf16", batch=128, num_q_heads=64,
+        num_kv_heads=8, head_dim=128, block_size=1024, query_len=2, windows=(4096, 0),
+        scale=1.0 / math.sqrt(128.0), seed=5, max_blocks_per_seq=64,
+        max_seq_len=65536, len_range=(2048, 65536),
+        description="large-block mixed-window MTP decode bf16: B=128, 64/8 heads, "
+                    "D=128, bs=1024, context U[2048, 65536], q_len 2, window 4096 / 0"),
+}
+
+
+def torch_dtype(name: str) -> torch.dtype:
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[name]
+
+
+@dataclass
+class Case:
+    """One realised input set; tensors live on ``device``."""
+    w: Workload
+    window: int
+    q: torch.Tensor
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    block_tables: torch.Tensor
+    seq_lens: torch.Tensor
+    query_lens: torch.Tensor
+    seq_lens_host: list
+    query_lens_host: list
+    tables_host: torch.Tensor
+    used_blocks: list           # per sequence, physical ids in logical order
+    unused_blocks: list
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def scale(self) -> float:
+        return self.w.scale
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.k_cache.shape[0])
+
+    def new_out(self) -> torch.Tensor:
+        return torch.empty_like(self.q)
+
+
+def _lengths(w: Workload, g: torch.Generator) -> tuple[list, list]:
+    if w.seq_lens:
+        lens = [int(x) for x in w.seq_lens]
+    else:
+        lo, hi = w.len_range
+        lens = [int(x) for x in torch.randint(lo, hi + 1, (w.batch,), generator=g)]
+    if w.query_lens:
+        qls = [int(x) for x in w.query_lens]
+    else:
+        qls = [w.query_len] * w.batch
+    return lens, qls
+
+
+def _fill_normal(t: torch.Tensor, gen: torch.Generator, chunk_elems: int = 1 << 28):
+    """Fill ``t`` with N(0,1) drawn in float32 then rounded to t.dtype."""
+    flat = t.view(-1)
+    n = flat.numel()
+    i = 0
+    while i < n:
+        m = min(chunk_elems, n - i)
+        flat[i:i + m] = torch.randn(m, generator=gen, device=t.device, dtype=torch.float32)
+        i += m
+
+
+def make_case(w: Workload | str, device="cpu", window: int | None = None,
+              poison: bool = True, q_gain: float = 1.0) -> Case:
+    """Build the seeded inputs of workload ``w`` on ``device``.
+
+    ``q_gain`` multiplies Q before rounding (a "peaked" variant with larger
+    logits); ``window`` defaults to the workload's first window.
+    """
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    if window is None:
+        window = w.windows[0]
+    g = torch.Generator(device="cpu").manual_seed(w.seed)
+    lens, qls = _lengths(w, g)
+    bs = w.block_size
+    nblk = [-(-L // bs) for L in lens]
+    needed = sum(nblk)
+    pool = w.pool if w.pool else math.ceil(1.25 * needed)
+    pool = max(pool, needed + 1)           # keep one unused block for table padding
+    perm = torch.randperm(pool, generator=g).tolist()
+    used, off = [], 0
+    for n in nblk:
+        used.append(perm[off:off + n])
+        off += n
+    unused = perm[needed:]
+    tables = torch.full((w.batch, w.max_blocks_per_seq), unused[0], dtype=torch.int32)
+    for b, ids in enumerate(used):
+        if len(ids) > w.max_blocks_per_seq:
+            raise ValueError("max_blocks_per_seq too small for the drawn lengths")
+        if ids:
+            tables[b, :len(ids)] = torch.tensor(ids, dtype=torch.int32)
+
+    dt = torch_dtype(w.dtype)
+    dev = torch.device(device)
+    vg = torch.Generator(device=dev).manual_seed(w.seed * 7919 + 17)
+    T = sum(qls)
+    q = torch.empty((T, w.num_q_heads, w.head_dim), dtype=dt, device=dev)
+    _fill_normal(q, vg)
+    if q_gain != 1.0:
+        q.copy_((q.float() * q_gain).to(dt))
+    k = torch.empty((pool, w.num_kv_heads, bs, w.head_dim), dtype=dt, device=dev)
+    v = torch.empty((pool, w.num_kv_heads, w.head_dim, bs), dtype=dt, device=dev)
+    _fill_normal(k, vg)
+    _fill_normal(v, vg)
+    if poison:
+        if unused:
+            ids = torch.tensor(unused, dtype=torch.long, device=dev)
+            k.index_fill_(0, ids, float("nan"))
+            v.index_fill_(0, ids, float("nan"))
+        for b, L in enumerate(lens):
+            tail = L % bs
+            if tail and used[b]:
+                last = used[b][-1]
+                k[last, :, tail:, :] = float("nan")
+                v[last, :, :, tail:] = float("nan")
+    return Case(
+        w=w, window=int(window), q=q, k_cache=k, v_cache=v,
+        block_tables=tables.to(dev), seq_lens=torch.tensor(lens, dtype=torch.int32, device=dev),
+        query_lens=torch.tensor(qls, dtype=torch.int32, device=dev),
+        seq_lens_host=lens, query_lens_host=qls, tables_host=tables,
+        used_blocks=used, unused_blocks=unused)
+
+
+def custom(name="custom", **kw) -> Workload:
+    """A workload built from keyword overrides of the tiny fp32 one."""
+    base = WORKLOADS["tiny_f32"]
+    kw.setdefault("name", name)
+    return replace(base, **kw)
