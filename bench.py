@@ -1,0 +1,242 @@
+"""Benchmark of one paged-attention decode call on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--window W]
+                    [--no-cpu-baseline] [--flush] [--path auto|mfma|valu] [--part-size P]
+
+A step is one pa_decode call (partition kernel + LSE reduce) over the
+workload's batch, inputs resident in HBM.  Prints ONE JSON line: µs per call,
+achieved HBM GB/s of the partition kernel on algorithmic bytes (HIP events
+recorded by the library around that kernel, on its stream), the roofline
+fraction of MI355X's 8 TB/s, and the float64 CPU oracle timed on a bounded
+sample of the same workload.
+
+Algorithmic bytes per call (what the method must move): for every
+(sequence, KV head) the K and V bytes of the union of its rows' visible
+positions, plus Q read, output write, the block-table entries of blocks that
+hold visible positions, and the two length arrays.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs per paged-decode call + achieved HBM GB/s (fraction of MI355X peak)"
+PEAK_GBPS = 8000.0
+DEFAULT_WORKLOAD = "gqa_bf16"
+
+
+def kernel_source_hash() -> str:
+    d = os.path.join(ROOT, "decode_attention_pa_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".h", ".hip")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(case) -> dict:
+    """Bytes the method must move for one call (see module docstring)."""
+    w = case.w
+    s = 2 if w.dtype == "bf16" else 4
+    kv = 0
+    tables = 0
+    bs = w.block_size
+    for L, q in zip(case.seq_lens_host, case.query_lens_host):
+        if q <= 0:
+            continue
+        lo = 0 if case.window == 0 else max(0, L - q + 1 - case.window)
+        kv += w.num_kv_heads * (L - lo) * w.head_dim * 2 * s
+        tables += 4 * ((L - 1) // bs - lo // bs + 1)
+    T = sum(case.query_lens_host)
+    qb = T * w.num_q_heads * w.head_dim * s
+    lens = 8 * w.batch
+    return dict(kv=kv, q=qb, out=qb, tables=tables, lens=lens,
+                total=kv + 2 * qb + tables + lens,
+                partition_kernel=kv + qb + tables + lens)
+
+
+def load_traffic(workload: str, window: int):
+    """HBM traffic of the partition kernel from the committed rocprofv3 counter
+    record, or None if absent or taken on different kernel sources."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p)).get(f"{workload}:w{window}")
+    if not rec or rec.get("kernel_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(case, out_gpu, budget_s: float, per_call_bytes: int) -> dict:
+    """The float64 oracle, as it stands, on a bounded sample of the workload's
+    sequences (host cores of this machine), scaled to µs per full call by
+    algorithmic KV bytes.  Also checks the GPU output on the sampled rows."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import paged_attention as ref
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from tests._gpu_util import oracle_inputs
+
+    w = case.w
+    order = list(range(w.batch))
+    done, t_total, bytes_done = [], 0.0, 0
+    max_err = 0.0
+    s = 2 if w.dtype == "bf16" else 4
+    with threadpool_limits(limits=1):
+        for b in order:
+            inp, rows = oracle_inputs(case, [b])
+            t0 = time.perf_counter()
+            exp = ref.decode(**inp)
+            t_total += time.perf_counter() - t0
+            L, q = case.seq_lens_host[b], case.query_lens_host[b]
+            lo = 0 if case.window == 0 else max(0, L - q + 1 - case.window)
+            bytes_done += w.num_kv_heads * (L - lo) * w.head_dim * 2 * s
+            got = out_gpu.float().cpu().numpy()[rows].astype(np.float64)
+            max_err = max(max_err, float(np.abs(got - exp).max()))
+            done.append(b)
+            if t_total >= budget_s:
+                break
+    kv_total = algorithmic_bytes(case)["kv"]
+    scale = kv_total / max(bytes_done, 1)
+    return dict(value=round(t_total * scale * 1e6, 1), unit="us/call", cores=1, kind="oracle",
+                sample=f"{len(done)} of {w.batch} sequences ({bytes_done / 1e6:.1f} MB of "
+                       f"{kv_total / 1e6:.1f} MB KV), float64 NumPy, 1 BLAS thread, "
+                       f"{t_total:.2f} s, scaled by KV bytes",
+                gbps=round(bytes_done / max(t_total, 1e-9) / 1e9, 3),
+                parity_max_abs=max_err)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--window", type=int, default=None)
+    ap.add_argument("--path", default="auto", choices=["auto", "mfma", "valu"])
+    ap.add_argument("--part-size", type=int, default=0)
+    ap.add_argument("--waves", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--flush", action="store_true",
+                    help="overwrite a 1 GiB buffer before every call (outside the call's events)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run plain 1 GiB device copies (counter calibration)")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); this library has no "
+              "multi-GPU path.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import decode_attention_pa_amd as pa
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    w = workloads.WORKLOADS[a.workload]
+    window = w.windows[0] if a.window is None else a.window
+    case = workloads.make_case(w, device="cuda", window=window)
+    out = torch.empty_like(case.q)
+    path = {"auto": 0, "valu": pa.PATH_VALU, "mfma": pa.PATH_MFMA}[a.path]
+    call = pa.Prepared(out, case.q, case.k_cache, case.v_cache, case.block_tables, case.seq_lens,
+                       case.query_lens, case.scale, window, w.num_kv_heads, w.block_size,
+                       max_seq_len=w.max_seq_len, max_query_len=w.query_len, path=path,
+                       part_size=a.part_size, waves=a.waves)
+    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda") if a.flush else None
+    if a.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    nb = algorithmic_bytes(case)
+    for _ in range(a.warmup):
+        call()
+    torch.cuda.synchronize()
+
+    K = a.steps
+    kb = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ke = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    cb = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ce = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(K):
+        if flush_buf is not None:
+            flush_buf.fill_(float(i))
+        call.set_events(kb[i], ke[i])
+        cb[i].record(stream)
+        call()
+        ce[i].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(stop)
+    kern_ms = sorted(kb[i].elapsed_time(ke[i]) for i in range(K))
+    call_ms = sorted(cb[i].elapsed_time(ce[i]) for i in range(K))
+    kern_avg = sum(kern_ms) / K
+    call_avg = sum(call_ms) / K
+    us_per_call = (call_avg if a.flush else total_ms / K) * 1e3
+    achieved = nb["partition_kernel"] / (kern_avg * 1e-3) / 1e9
+    call_gbps = nb["total"] / (us_per_call * 1e-6) / 1e9
+    traffic = load_traffic(a.workload, window)
+
+    res = {
+        "metric": METRIC,
+        "value": round(us_per_call, 2),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": a.warmup,
+        "ms_per_step": round(total_ms / K, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "description": w.description, "window": window,
+            "batch": w.batch, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim, "block_size": w.block_size, "query_len": w.query_len,
+            "realised_context_tokens": sum(case.seq_lens_host), "plan": call.plan,
+            "flush_between_calls": bool(a.flush),
+        },
+        "achieved_gbps_per_call": round(call_gbps, 1),
+        "frac_of_peak_per_call": round(call_gbps / PEAK_GBPS, 4),
+        "algorithmic_bytes": nb,
+        "kernel_us": {"partition_avg": round(kern_avg * 1e3, 2),
+                      "partition_p10": round(kern_ms[K // 10] * 1e3, 2),
+                      "partition_p90": round(kern_ms[(9 * K) // 10] * 1e3, 2),
+                      "call_avg": round(call_avg * 1e3, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic},
+        "host_wall_s": round(wall, 3),
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(case, out, a.cpu_budget, nb["total"])
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

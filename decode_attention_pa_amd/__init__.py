@@ -1,0 +1,299 @@
+"""Python binding of libpa_decode.so (paged-attention decode on MI355X).
+
+Argument marshalling only: torch tensors supply device memory and the
+current HIP stream; every step of the computation runs in the library's HIP
+kernels.  There is no fallback: if the library is not built, or a call
+fails, an exception says so.
+
+    import decode_attention_pa_amd as pa
+    pa.decode(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens,
+              scale, window, num_kv_heads, block_size, max_seq_len=...)
+
+Layouts (see include/pa_decode.h): q/out [T, H_q, D]; k_cache
+[num_blocks, H_kv, block_size, D]; v_cache [num_blocks, H_kv, D, block_size];
+block_tables int32 [B, max_blocks_per_seq]; seq_lens, query_lens int32 [B].
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "PaError", "Dims", "Plan", "Options", "load", "library_path", "plan", "workspace_size",
+    "decode", "debug_spans", "PATH_AUTO", "PATH_VALU", "PATH_MFMA", "F32", "BF16",
+    "EXPORTED_SYMBOLS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libpa_decode.so")
+
+PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
+F32, BF16 = 0, 1
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
+
+EXPORTED_SYMBOLS = (
+    "pa_plan_compute", "pa_decode_workspace_size", "pa_decode_workspace_size_ex",
+    "pa_decode", "pa_decode_ex", "pa_debug_spans", "pa_status_string", "pa_last_error",
+)
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("max_query_len", ctypes.c_int32),
+                ("max_seq_len", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("rows", ctypes.c_int32),
+                ("span_max", ctypes.c_int32), ("part_size", ctypes.c_int32),
+                ("num_parts", ctypes.c_int32), ("waves", ctypes.c_int32),
+                ("one_shot", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_uint64)]
+
+    def as_dict(self) -> dict:
+        return {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+
+
+class Options(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("part_size", ctypes.c_int32),
+                ("waves", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("event_begin", ctypes.c_void_p), ("event_end", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Loads the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise PaError(ERR_UNSUPPORTED,
+                      f"{_LIB_PATH} is not built; run `python -m decode_attention_pa_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    I32 = ctypes.c_int32
+    pd = ctypes.POINTER(Dims)
+    po = ctypes.POINTER(Options)
+    lib.pa_plan_compute.argtypes = [pd, I32, I32, I32, I32, po, ctypes.POINTER(Plan)]
+    lib.pa_decode_workspace_size_ex.argtypes = [pd, I32, I32, I32, po, ctypes.POINTER(ctypes.c_size_t)]
+    lib.pa_decode_workspace_size.argtypes = [pd, I32, I32, I32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.pa_decode.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, I32, I32, I32, pd, P,
+                              ctypes.c_size_t, P]
+    lib.pa_decode_ex.argtypes = lib.pa_decode.argtypes + [po]
+    lib.pa_debug_spans.argtypes = [P, P, P, I32, I32, I32, pd, po, P, P, P, P, P]
+    lib.pa_status_string.argtypes = [I32]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_last_error.argtypes = []
+    lib.pa_last_error.restype = ctypes.c_char_p
+    for name in ("pa_plan_compute", "pa_decode_workspace_size", "pa_decode_workspace_size_ex",
+                 "pa_decode", "pa_decode_ex", "pa_debug_spans"):
+        getattr(lib, name).restype = I32
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != OK:
+        lib = load()
+        raise PaError(status, f"{lib.pa_status_string(status).decode()}: "
+                              f"{lib.pa_last_error().decode()}")
+
+
+def make_dims(batch, num_q_heads, head_dim, max_query_len, max_seq_len, max_blocks_per_seq,
+              num_blocks, dtype) -> Dims:
+    return Dims(int(batch), int(num_q_heads), int(head_dim), int(max_query_len),
+                int(max_seq_len), int(max_blocks_per_seq), int(num_blocks), int(dtype))
+
+
+def make_options(path=0, part_size=0, waves=0, event_begin=None, event_end=None) -> Options:
+    return Options(int(path), int(part_size), int(waves), 0,
+                   _event_handle(event_begin), _event_handle(event_end))
+
+
+def _event_handle(ev):
+    if ev is None:
+        return None
+    return ctypes.c_void_p(int(ev.cuda_event) if hasattr(ev, "cuda_event") else int(ev))
+
+
+def plan(dims: Dims, window: int, num_kv_heads: int, block_size: int, num_cus: int = 256,
+         **opts) -> dict:
+    """The launch plan the library would use (no device needed)."""
+    p = Plan()
+    o = make_options(**opts)
+    _check(load().pa_plan_compute(ctypes.byref(dims), int(window), int(num_kv_heads),
+                                  int(block_size), int(num_cus), ctypes.byref(o), ctypes.byref(p)))
+    return p.as_dict()
+
+
+def workspace_size(dims: Dims, window: int, num_kv_heads: int, block_size: int, **opts) -> int:
+    n = ctypes.c_size_t(0)
+    o = make_options(**opts)
+    _check(load().pa_decode_workspace_size_ex(ctypes.byref(dims), int(window), int(num_kv_heads),
+                                              int(block_size), ctypes.byref(o), ctypes.byref(n)))
+    return int(n.value)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise PaError(ERR_INVALID_ARG, f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(int(stream.cuda_stream))
+
+
+def dims_for(q, k_cache, block_tables, max_query_len, max_seq_len) -> Dims:
+    T, Hq, D = q.shape
+    return make_dims(block_tables.shape[0], Hq, D, max_query_len, max_seq_len,
+                     block_tables.shape[1], k_cache.shape[0], _dtype_code(q))
+
+
+def _validate(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, num_kv_heads, block_size):
+    import torch
+    for name, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("block_tables", block_tables), ("seq_lens", seq_lens),
+                    ("query_lens", query_lens)):
+        if not isinstance(t, torch.Tensor):
+            raise PaError(ERR_INVALID_ARG, f"{name} must be a torch.Tensor")
+        if t.device.type != "cuda":
+            raise PaError(ERR_INVALID_ARG, f"{name} must be on the GPU")
+        if not t.is_contiguous():
+            raise PaError(ERR_INVALID_ARG, f"{name} must be contiguous")
+    for name, t in (("block_tables", block_tables), ("seq_lens", seq_lens), ("query_lens", query_lens)):
+        if t.dtype != torch.int32:
+            raise PaError(ERR_INVALID_ARG, f"{name} must be int32")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype == out.dtype):
+        raise PaError(ERR_INVALID_ARG, "q, k_cache, v_cache and out must share one dtype")
+    if q.dim() != 3 or out.shape != q.shape:
+        raise PaError(ERR_INVALID_ARG, "q and out must be [T, H_q, D] of one shape")
+    T, Hq, D = q.shape
+    nb = k_cache.shape[0]
+    if tuple(k_cache.shape) != (nb, num_kv_heads, block_size, D):
+        raise PaError(ERR_INVALID_ARG, f"k_cache must be [num_blocks, {num_kv_heads}, {block_size}, {D}]")
+    if tuple(v_cache.shape) != (nb, num_kv_heads, D, block_size):
+        raise PaError(ERR_INVALID_ARG, f"v_cache must be [num_blocks, {num_kv_heads}, {D}, {block_size}]")
+    B = block_tables.shape[0]
+    if block_tables.dim() != 2 or seq_lens.shape != (B,) or query_lens.shape != (B,):
+        raise PaError(ERR_INVALID_ARG, "block_tables [B, M], seq_lens [B], query_lens [B]")
+
+
+def decode(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, scale, window,
+           num_kv_heads, block_size, max_seq_len, max_query_len=None, workspace=None,
+           stream=None, path=0, part_size=0, waves=0, event_begin=None, event_end=None):
+    """Runs pa_decode_ex on torch tensors; returns ``out``.
+
+    ``max_seq_len`` / ``max_query_len`` are host-known upper bounds of the
+    device arrays ``seq_lens`` / ``query_lens`` (the library never reads
+    device memory from the host).  ``workspace`` (uint8 CUDA tensor) is
+    allocated when not given and needed.
+    """
+    import torch
+    _validate(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, num_kv_heads, block_size)
+    if max_query_len is None:
+        max_query_len = int(q.shape[0]) if block_tables.shape[0] else 1
+        max_query_len = max(1, min(max_query_len, int(max_seq_len)))
+    dims = dims_for(q, k_cache, block_tables, max_query_len, max_seq_len)
+    opts = make_options(path, part_size, waves, event_begin, event_end)
+    need = workspace_size(dims, window, num_kv_heads, block_size, path=path,
+                          part_size=part_size, waves=waves)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().pa_decode_ex(
+        ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(q.data_ptr()),
+        ctypes.c_void_p(k_cache.data_ptr()), ctypes.c_void_p(v_cache.data_ptr()),
+        ctypes.c_void_p(block_tables.data_ptr()), ctypes.c_void_p(seq_lens.data_ptr()),
+        ctypes.c_void_p(query_lens.data_ptr()), ctypes.c_float(scale), int(window),
+        int(num_kv_heads), int(block_size), ctypes.byref(dims), ws_ptr, ws_bytes,
+        _stream_handle(stream), ctypes.byref(opts)))
+    return out
+
+
+def debug_spans(block_tables, seq_lens, query_lens, window, num_kv_heads, block_size, dims: Dims,
+                total_q: int, stream=None, **opts) -> dict:
+    """Index facts from the kernels' own helpers (see pa_debug_spans)."""
+    import torch
+    p = plan(dims, window, num_kv_heads, block_size, **opts)
+    dev = block_tables.device
+    B = dims.batch
+    seq_info = torch.full((B, 4), -7, dtype=torch.int32, device=dev)
+    row_info = torch.full((max(total_q, 1), 2), -7, dtype=torch.int32, device=dev)
+    blocks = torch.full((B, dims.max_blocks_per_seq), -7, dtype=torch.int32, device=dev)
+    parts = torch.full((B, p["num_parts"], 2), -7, dtype=torch.int32, device=dev)
+    o = make_options(**opts)
+    _check(load().pa_debug_spans(
+        ctypes.c_void_p(block_tables.data_ptr()), ctypes.c_void_p(seq_lens.data_ptr()),
+        ctypes.c_void_p(query_lens.data_ptr()), int(window), int(num_kv_heads), int(block_size),
+        ctypes.byref(dims), ctypes.byref(o), ctypes.c_void_p(seq_info.data_ptr()),
+        ctypes.c_void_p(row_info.data_ptr()), ctypes.c_void_p(blocks.data_ptr()),
+        ctypes.c_void_p(parts.data_ptr()), _stream_handle(stream)))
+    return dict(seq_info=seq_info, row_info=row_info[:total_q], blocks=blocks, parts=parts, plan=p)
+
+
+class Prepared:
+    """A pa_decode_ex call with its arguments marshalled once.
+
+    For timing loops: ``__call__`` re-issues the same call (same tensors, same
+    stream) with only the ctypes call itself on the host path.  Tensors must
+    stay alive while the object is used.
+    """
+
+    def __init__(self, out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, scale, window,
+                 num_kv_heads, block_size, max_seq_len, max_query_len, workspace=None,
+                 stream=None, path=0, part_size=0, waves=0, event_begin=None, event_end=None):
+        import torch
+        _validate(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, num_kv_heads,
+                  block_size)
+        self.dims = dims_for(q, k_cache, block_tables, max_query_len, max_seq_len)
+        self.opts = make_options(path, part_size, waves, event_begin, event_end)
+        self.plan = plan(self.dims, window, num_kv_heads, block_size,
+                         num_cus=torch.cuda.get_device_properties(q.device).multi_processor_count,
+                         path=path, part_size=part_size, waves=waves)
+        need = workspace_size(self.dims, window, num_kv_heads, block_size, path=path,
+                              part_size=part_size, waves=waves)
+        if workspace is None and need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        self.workspace = workspace
+        self._keep = (out, q, k_cache, v_cache, block_tables, seq_lens, query_lens)
+        vp = ctypes.c_void_p
+        self.args = (
+            vp(out.data_ptr()), vp(q.data_ptr()), vp(k_cache.data_ptr()), vp(v_cache.data_ptr()),
+            vp(block_tables.data_ptr()), vp(seq_lens.data_ptr()), vp(query_lens.data_ptr()),
+            ctypes.c_float(scale), int(window), int(num_kv_heads), int(block_size),
+            ctypes.byref(self.dims),
+            vp(workspace.data_ptr()) if workspace is not None else None,
+            workspace.numel() if workspace is not None else 0,
+            _stream_handle(stream), ctypes.byref(self.opts))
+        self._fn = load().pa_decode_ex
+
+    def set_events(self, event_begin, event_end):
+        self.opts.event_begin = _event_handle(event_begin)
+        self.opts.event_end = _event_handle(event_end)
+
+    def __call__(self):
+        st = self._fn(*self.args)
+        if st:
+            _check(st)

@@ -1,0 +1,56 @@
+"""Builds libpa_decode.so (gfx950) in-tree with hipcc.
+
+Usage: python -m decode_attention_pa_amd.build [--debug]
+"""
+
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB = os.path.join(HERE, "libpa_decode.so")
+SOURCES = [os.path.join(HERE, "csrc", "pa_decode.hip")]
+HEADERS = [os.path.join(ROOT, "include", "pa_decode.h")] + [
+    os.path.join(HERE, "csrc", f) for f in sorted(os.listdir(os.path.join(HERE, "csrc")))
+    if f.endswith(".h")]
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", "hipcc"):
+        if c and (os.path.isabs(c) and os.path.exists(c) or not os.path.isabs(c)):
+            return c
+    return "hipcc"
+
+
+def command(out: str = LIB, extra=()) -> list[str]:
+    return [
+        hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+        # packed fp32 VALU ops stay off: plain fp32 code only
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wall", "-Wno-unused-function",
+        "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
+        *extra, *SOURCES, "-o", out,
+    ]
+
+
+def build(verbose: bool = True, extra=()) -> str:
+    tmp = LIB + ".tmp"
+    cmd = command(tmp, extra)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(extra=["-DPA_DEBUG_CHECKS"] if "--debug" in sys.argv else ())

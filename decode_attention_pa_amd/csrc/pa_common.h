@@ -1,0 +1,124 @@
+// Shared device/host helpers of the paged-attention decode kernels (gfx950).
+//
+// Index arithmetic lives here once so that the partition kernels, the LSE
+// reduce and the index-dump kernel agree bit for bit.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Positions per inner step of every partition kernel.  Partitions start on
+// multiples of this (relative to the aligned start of the span), so a chunk
+// never straddles two partitions.
+constexpr int kChunk = 32;
+
+// First position query token i may see.  gllm "feat(backend): sliding-window
+// PagedAttention" (#116): window w > 0 shows positions p-w+1 .. p to the
+// token at p; w == 0 is unlimited causal.  The query tokens are the last q of
+// the L-position context, so token i sits at p = L - q + i.
+__host__ __device__ inline int first_visible(int L, int q, int i, int window) {
+  const int p = L - q + i;
+  return window == 0 ? 0 : max(0, p + 1 - window);
+}
+
+// Union of a sequence's visible ranges and its partition grid.
+//   [lo, hi)  positions some query token of the sequence can see
+//   base      lo rounded down to a chunk boundary; partition j covers
+//             [max(lo, base + j*P), min(hi, base + (j+1)*P))
+//   nparts    number of non-empty partitions (0 when q == 0)
+struct SeqView {
+  int lo, hi, base, nparts;
+};
+
+__host__ __device__ inline SeqView seq_view(int L, int q, int window, int part_size) {
+  SeqView s;
+  if (q <= 0 || L <= 0) {
+    s.lo = s.hi = L > 0 ? L : 0;
+    s.base = s.lo & ~(kChunk - 1);
+    s.nparts = 0;
+    return s;
+  }
+  s.lo = first_visible(L, q, 0, window);
+  s.hi = L;
+  s.base = s.lo & ~(kChunk - 1);
+  s.nparts = (s.hi - s.base + part_size - 1) / part_size;
+  return s;
+}
+
+__host__ __device__ inline void partition_range(const SeqView& s, int j, int part_size,
+                                                int* ps, int* pe) {
+  *ps = max(s.lo, s.base + j * part_size);
+  *pe = min(s.hi, s.base + (j + 1) * part_size);
+}
+
+// Physical block holding position t of a sequence whose block-table row is
+// `table_row`; block_size = 1 << log2_bs.
+__device__ inline int phys_block(const int32_t* __restrict__ table_row, int t, int log2_bs) {
+  return table_row[t >> log2_bs];
+}
+
+// Exclusive prefix sum of query_lens[0 .. b) computed by one wave; every lane
+// returns the sum.  Gives the first q/out row of sequence b in the packed
+// [sum q_b, H_q, D] layout.
+__device__ inline int wave_row_offset(const int32_t* __restrict__ query_lens, int b) {
+  const int lane = threadIdx.x & 63;
+  int s = 0;
+  for (int k = lane; k < b; k += 64) s += query_lens[k];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  return s;
+}
+
+__device__ inline float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Arguments shared by the partition kernels.
+struct PartArgs {
+  void* out;                   // [T, H_q, D] (one-shot sequences)
+  const void* q;               // [T, H_q, D]
+  const void* k_cache;         // [num_blocks, H_kv, bs, D]
+  const void* v_cache;         // [num_blocks, H_kv, D, bs]
+  const int32_t* block_tables; // [B, max_blocks_per_seq]
+  const int32_t* seq_lens;     // [B]
+  const int32_t* query_lens;   // [B]
+  float* ws_m;                 // [B, H_kv, NP, R] running max, log2 domain
+  float* ws_l;                 // [B, H_kv, NP, R] exp-sum
+  float* ws_o;                 // [B, H_kv, NP, R, D] normalised partial output
+  float scale_log2;            // scale * log2(e)
+  int window;
+  int num_q_heads;
+  int num_kv_heads;
+  int group;                   // G = H_q / H_kv
+  int rows;                    // R = G * max_query_len (workspace row stride)
+  int num_parts;               // NP (workspace partition stride)
+  int part_size;               // P, multiple of kChunk * waves
+  int log2_bs;
+  int max_blocks_per_seq;
+};
+
+struct ReduceArgs {
+  void* out;
+  const int32_t* seq_lens;
+  const int32_t* query_lens;
+  const float* ws_m;
+  const float* ws_l;
+  const float* ws_o;
+  int window;
+  int num_q_heads;
+  int num_kv_heads;
+  int group;
+  int rows;
+  int num_parts;
+  int part_size;
+};
+
+}  // namespace pa

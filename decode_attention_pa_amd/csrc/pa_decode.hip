@@ -1,0 +1,405 @@
+// C ABI of the paged-attention decode library: validation, launch plan,
+// kernel dispatch.  Declarations and the full contract: include/pa_decode.h.
+#include "pa_decode.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
+#include "pa_common.h"
+#include "pa_mfma.h"
+#include "pa_reduce.h"
+#include "pa_valu.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pa_status fail(pa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+pa_status hip_fail(hipError_t e, const char* what) {
+  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool log_enabled() {
+  static const int on = [] {
+    const char* v = std::getenv("PA_LOG");
+    return (v && v[0] && v[0] != '0') ? 1 : 0;
+  }();
+  return on != 0;
+}
+
+int ilog2_exact(int x) {
+  if (x <= 0 || (x & (x - 1))) return -1;
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+// Host-visible argument checks shared by every entry point.
+pa_status check_shape(const pa_dims* d, int32_t window, int32_t num_kv_heads, int32_t block_size) {
+  if (!d) return fail(PA_ERR_INVALID_ARG, "dims is NULL");
+  if (d->batch < 0 || d->batch > 65535)
+    return fail(PA_ERR_INVALID_ARG, "batch %d outside [0, 65535]", d->batch);
+  if (d->dtype != PA_F32 && d->dtype != PA_BF16)
+    return fail(PA_ERR_INVALID_ARG, "dtype %d is neither PA_F32 nor PA_BF16", d->dtype);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", d->head_dim);
+  if (num_kv_heads < 1 || num_kv_heads > 65535)
+    return fail(PA_ERR_INVALID_ARG, "num_kv_heads %d outside [1, 65535]", num_kv_heads);
+  if (d->num_q_heads < 1 || d->num_q_heads % num_kv_heads)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                d->num_q_heads, num_kv_heads);
+  if (ilog2_exact(block_size) < 4 || block_size > 1024)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d must be a power of two in [16, 1024]", block_size);
+  if (window < 0) return fail(PA_ERR_INVALID_ARG, "window %d is negative", window);
+  if (d->max_query_len < 1) return fail(PA_ERR_INVALID_ARG, "max_query_len %d < 1", d->max_query_len);
+  if (d->max_seq_len < d->max_query_len)
+    return fail(PA_ERR_INVALID_ARG, "max_seq_len %d < max_query_len %d", d->max_seq_len,
+                d->max_query_len);
+  if (d->max_blocks_per_seq < cdiv(d->max_seq_len, block_size))
+    return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq %d < ceil(max_seq_len %d / block_size %d)",
+                d->max_blocks_per_seq, d->max_seq_len, block_size);
+  if (d->num_blocks < 1) return fail(PA_ERR_INVALID_ARG, "num_blocks %d < 1", d->num_blocks);
+  const int64_t rows = (int64_t)(d->num_q_heads / num_kv_heads) * d->max_query_len;
+  if (rows > 64)
+    return fail(PA_ERR_UNSUPPORTED, "rows per KV head G*max_query_len = %lld exceeds 64",
+                (long long)rows);
+  return PA_OK;
+}
+
+pa_status make_plan(const pa_dims* d, int32_t window, int32_t hkv, int32_t bs, int32_t num_cus,
+                    const pa_options* o, pa_plan* p) {
+  pa_status st = check_shape(d, window, hkv, bs);
+  if (st != PA_OK) return st;
+  if (!p) return fail(PA_ERR_INVALID_ARG, "plan is NULL");
+  if (num_cus < 1) return fail(PA_ERR_INVALID_ARG, "num_cus %d < 1", num_cus);
+  pa_plan r = {};
+  const int G = d->num_q_heads / hkv;
+  r.rows = G * d->max_query_len;
+  r.span_max = window ? (int32_t)std::min<int64_t>(d->max_seq_len, (int64_t)window + d->max_query_len - 1)
+                      : d->max_seq_len;
+  const int path_req = o ? o->path : PA_PATH_AUTO;
+  if (path_req < PA_PATH_AUTO || path_req > PA_PATH_MFMA)
+    return fail(PA_ERR_INVALID_ARG, "path %d unknown", path_req);
+  if (path_req == PA_PATH_AUTO) {
+    // fp32 inputs never take reduced-precision products.  For bf16 the matrix
+    // cores are the measured choice at every row count (kernels).
+    r.path = d->dtype == PA_F32 ? PA_PATH_VALU : PA_PATH_MFMA;
+  } else {
+    r.path = path_req;
+  }
+  if (r.path == PA_PATH_MFMA && d->dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "the matrix-core path needs bf16 inputs");
+  const int nrt = (r.rows + 15) / 16;
+  if (r.path == PA_PATH_MFMA) {
+    const int w_req = o ? o->waves : 0;
+    if (w_req) {
+      if (w_req != 1 && w_req != 2 && w_req != 4)
+        return fail(PA_ERR_INVALID_ARG, "waves %d must be 1, 2 or 4", w_req);
+      if (w_req * nrt > 4)
+        return fail(PA_ERR_UNSUPPORTED, "waves %d x row tiles %d exceeds 4", w_req, nrt);
+      r.waves = w_req;
+    } else {
+      r.waves = nrt == 1 ? 4 : (nrt == 2 ? 2 : 1);
+    }
+  } else {
+    r.waves = 4;  // 256-thread workgroup
+  }
+  const int64_t span_cover = (int64_t)r.span_max + pa::kChunk - 1;  // span plus alignment slack
+  const int p_req = o ? o->part_size : 0;
+  if (p_req) {
+    if (p_req < pa::kChunk || p_req % pa::kChunk)
+      return fail(PA_ERR_INVALID_ARG, "part_size %d must be a positive multiple of %d", p_req,
+                  pa::kChunk);
+    r.part_size = p_req;
+  } else {
+    // Enough partitions for ~ 2 workgroups per CU when every (sequence, KV
+    // head) has the longest span; partitions of at least 8 chunks so the
+    // partial-state traffic stays small, at most 64 chunks so that unequal
+    // sequence lengths do not leave a long tail.
+    const int64_t units = (int64_t)d->batch * hkv;
+    const int64_t chunks = cdiv(span_cover, pa::kChunk);
+    const int64_t want = std::max<int64_t>(1, cdiv(2 * (int64_t)num_cus, std::max<int64_t>(units, 1)));
+    int64_t pc = cdiv(chunks, want);
+    pc = std::max<int64_t>(pc, 8);
+    pc = std::min<int64_t>(pc, 64);
+    r.part_size = (int32_t)(pc * pa::kChunk);
+  }
+  r.num_parts = (int32_t)std::max<int64_t>(1, cdiv(span_cover, r.part_size));
+  if (r.num_parts == 1) r.part_size = (int32_t)(cdiv(span_cover, pa::kChunk) * pa::kChunk);
+  r.one_shot = r.num_parts == 1;
+  if (r.one_shot) {
+    r.workspace_bytes = 0;
+  } else {
+    const uint64_t states = (uint64_t)d->batch * hkv * r.num_parts * r.rows;
+    r.workspace_bytes = 2 * align256(states * 4) + align256(states * d->head_dim * 4);
+  }
+  *p = r;
+  return PA_OK;
+}
+
+std::atomic<int> g_cu_count[64];
+
+pa_status device_cu_count(int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(PA_ERR_HIP, "device ordinal %d out of range", dev);
+  int n = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(MultiprocessorCount)");
+    g_cu_count[dev].store(n, std::memory_order_relaxed);
+  }
+  *out = n;
+  return PA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+template <int D, int NRT, int NW>
+void launch_mfma_inst(dim3 grid, hipStream_t s, const pa::PartArgs& a) {
+  hipLaunchKernelGGL((pa::part_mfma<D, NRT, NW>), grid, dim3(64 * NW), 0, s, a);
+}
+
+template <int D>
+bool launch_mfma(int nrt, int nw, dim3 grid, hipStream_t s, const pa::PartArgs& a) {
+  switch (nrt * 8 + nw) {
+    case 1 * 8 + 1: launch_mfma_inst<D, 1, 1>(grid, s, a); return true;
+    case 1 * 8 + 2: launch_mfma_inst<D, 1, 2>(grid, s, a); return true;
+    case 1 * 8 + 4: launch_mfma_inst<D, 1, 4>(grid, s, a); return true;
+    case 2 * 8 + 1: launch_mfma_inst<D, 2, 1>(grid, s, a); return true;
+    case 2 * 8 + 2: launch_mfma_inst<D, 2, 2>(grid, s, a); return true;
+    case 3 * 8 + 1: launch_mfma_inst<D, 3, 1>(grid, s, a); return true;
+    case 4 * 8 + 1: launch_mfma_inst<D, 4, 1>(grid, s, a); return true;
+    default: return false;
+  }
+}
+
+pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* seq_lens, const int32_t* query_lens,
+              float scale, int32_t window, int32_t hkv, int32_t bs, const pa_dims* d,
+              void* workspace, size_t workspace_bytes, void* stream, const pa_options* o) {
+  pa_status st = check_shape(d, window, hkv, bs);
+  if (st != PA_OK) return st;
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens || !query_lens)
+    return fail(PA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return fail(PA_ERR_INVALID_ARG, "out, q, k_cache and v_cache must be 16-byte aligned");
+  if (!aligned(block_tables, 4) || !aligned(seq_lens, 4) || !aligned(query_lens, 4))
+    return fail(PA_ERR_INVALID_ARG, "int32 arrays must be 4-byte aligned");
+  if (workspace && !aligned(workspace, 16))
+    return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (d->batch == 0) return PA_OK;
+  int cus = 0;
+  st = device_cu_count(&cus);
+  if (st != PA_OK) return st;
+  pa_plan p;
+  st = make_plan(d, window, hkv, bs, cus, o, &p);
+  if (st != PA_OK) return st;
+  if (p.workspace_bytes && (!workspace || workspace_bytes < p.workspace_bytes))
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes given, %llu needed", workspace ? workspace_bytes : 0,
+                (unsigned long long)p.workspace_bytes);
+  if (log_enabled())
+    std::fprintf(stderr,
+                 "[pa_decode] B=%d Hq=%d Hkv=%d D=%d bs=%d w=%d R=%d span_max=%d path=%s P=%d NP=%d "
+                 "waves=%d one_shot=%d ws=%llu cus=%d\n",
+                 d->batch, d->num_q_heads, hkv, d->head_dim, bs, window, p.rows, p.span_max,
+                 p.path == PA_PATH_MFMA ? "mfma" : "valu", p.part_size, p.num_parts, p.waves,
+                 p.one_shot, (unsigned long long)p.workspace_bytes, cus);
+
+  const uint64_t states = (uint64_t)d->batch * hkv * p.num_parts * p.rows;
+  char* ws = (char*)workspace;
+  pa::PartArgs a = {};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.query_lens = query_lens;
+  a.ws_m = p.one_shot ? nullptr : (float*)ws;
+  a.ws_l = p.one_shot ? nullptr : (float*)(ws + align256(states * 4));
+  a.ws_o = p.one_shot ? nullptr : (float*)(ws + 2 * align256(states * 4));
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.window = window;
+  a.num_q_heads = d->num_q_heads;
+  a.num_kv_heads = hkv;
+  a.group = d->num_q_heads / hkv;
+  a.rows = p.rows;
+  a.num_parts = p.num_parts;
+  a.part_size = p.part_size;
+  a.log2_bs = ilog2_exact(bs);
+  a.max_blocks_per_seq = d->max_blocks_per_seq;
+
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (o && o->event_begin) {
+    e = hipEventRecord((hipEvent_t)o->event_begin, s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(begin)");
+  }
+  const dim3 grid(p.num_parts, hkv, d->batch);
+  const int nrt = (p.rows + 15) / 16;
+  bool ok = true;
+  if (p.path == PA_PATH_MFMA) {
+    ok = d->head_dim == 64 ? launch_mfma<64>(nrt, p.waves, grid, s, a)
+                           : launch_mfma<128>(nrt, p.waves, grid, s, a);
+  } else if (d->dtype == PA_F32) {
+    if (d->head_dim == 64) hipLaunchKernelGGL((pa::part_valu<float, 64>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((pa::part_valu<float, 128>), grid, dim3(256), 0, s, a);
+  } else {
+    if (d->head_dim == 64) hipLaunchKernelGGL((pa::part_valu<uint16_t, 64>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((pa::part_valu<uint16_t, 128>), grid, dim3(256), 0, s, a);
+  }
+  if (!ok) return fail(PA_ERR_UNSUPPORTED, "no kernel for %d row tiles x %d waves", nrt, p.waves);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "partition kernel launch");
+  if (o && o->event_end) {
+    e = hipEventRecord((hipEvent_t)o->event_end, s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(end)");
+  }
+  if (!p.one_shot) {
+    pa::ReduceArgs r = {};
+    r.out = out;
+    r.seq_lens = seq_lens;
+    r.query_lens = query_lens;
+    r.ws_m = a.ws_m;
+    r.ws_l = a.ws_l;
+    r.ws_o = a.ws_o;
+    r.window = window;
+    r.num_q_heads = d->num_q_heads;
+    r.num_kv_heads = hkv;
+    r.group = a.group;
+    r.rows = p.rows;
+    r.num_parts = p.num_parts;
+    r.part_size = p.part_size;
+    const dim3 rgrid(p.rows, hkv, d->batch);
+    if (d->dtype == PA_F32) {
+      if (d->head_dim == 64) hipLaunchKernelGGL((pa::lse_reduce<float, 64>), rgrid, dim3(256), 0, s, r);
+      else hipLaunchKernelGGL((pa::lse_reduce<float, 128>), rgrid, dim3(256), 0, s, r);
+    } else {
+      if (d->head_dim == 64) hipLaunchKernelGGL((pa::lse_reduce<uint16_t, 64>), rgrid, dim3(256), 0, s, r);
+      else hipLaunchKernelGGL((pa::lse_reduce<uint16_t, 128>), rgrid, dim3(256), 0, s, r);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "reduce kernel launch");
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_plan_compute(const pa_dims* dims, int32_t window, int32_t num_kv_heads,
+                          int32_t block_size, int32_t num_cus, const pa_options* opts,
+                          pa_plan* plan) {
+  return make_plan(dims, window, num_kv_heads, block_size, num_cus, opts, plan);
+}
+
+pa_status pa_decode_workspace_size_ex(const pa_dims* dims, int32_t window, int32_t num_kv_heads,
+                                      int32_t block_size, const pa_options* opts, size_t* bytes) {
+  if (!bytes) return fail(PA_ERR_INVALID_ARG, "bytes is NULL");
+  pa_status st = check_shape(dims, window, num_kv_heads, block_size);
+  if (st != PA_OK) return st;
+  int cus = 0;
+  st = device_cu_count(&cus);
+  if (st != PA_OK) return st;
+  pa_plan p;
+  st = make_plan(dims, window, num_kv_heads, block_size, cus, opts, &p);
+  if (st != PA_OK) return st;
+  *bytes = (size_t)p.workspace_bytes;
+  return PA_OK;
+}
+
+pa_status pa_decode_workspace_size(const pa_dims* dims, int32_t window, int32_t num_kv_heads,
+                                   int32_t block_size, size_t* bytes) {
+  return pa_decode_workspace_size_ex(dims, window, num_kv_heads, block_size, nullptr, bytes);
+}
+
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* seq_lens,
+                    const int32_t* query_lens, float scale, int32_t window,
+                    int32_t num_kv_heads, int32_t block_size, const pa_dims* dims,
+                    void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return run(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, scale, window,
+             num_kv_heads, block_size, dims, workspace, workspace_bytes, hip_stream, nullptr);
+}
+
+pa_status pa_decode_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* seq_lens,
+                       const int32_t* query_lens, float scale, int32_t window,
+                       int32_t num_kv_heads, int32_t block_size, const pa_dims* dims,
+                       void* workspace, size_t workspace_bytes, void* hip_stream,
+                       const pa_options* opts) {
+  return run(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, scale, window,
+             num_kv_heads, block_size, dims, workspace, workspace_bytes, hip_stream, opts);
+}
+
+pa_status pa_debug_spans(const int32_t* block_tables, const int32_t* seq_lens,
+                         const int32_t* query_lens, int32_t window, int32_t num_kv_heads,
+                         int32_t block_size, const pa_dims* dims, const pa_options* opts,
+                         int32_t* seq_info, int32_t* row_info, int32_t* blocks, int32_t* parts,
+                         void* hip_stream) {
+  pa_status st = check_shape(dims, window, num_kv_heads, block_size);
+  if (st != PA_OK) return st;
+  if (!block_tables || !seq_lens || !query_lens || !seq_info || !row_info || !blocks || !parts)
+    return fail(PA_ERR_INVALID_ARG, "a pointer is NULL");
+  if (dims->batch == 0) return PA_OK;
+  int cus = 0;
+  st = device_cu_count(&cus);
+  if (st != PA_OK) return st;
+  pa_plan p;
+  st = make_plan(dims, window, num_kv_heads, block_size, cus, opts, &p);
+  if (st != PA_OK) return st;
+  pa::SpanArgs a = {};
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.query_lens = query_lens;
+  a.seq_info = seq_info;
+  a.row_info = row_info;
+  a.blocks = blocks;
+  a.parts = parts;
+  a.window = window;
+  a.part_size = p.part_size;
+  a.num_parts = p.num_parts;
+  a.log2_bs = ilog2_exact(block_size);
+  a.max_blocks_per_seq = dims->max_blocks_per_seq;
+  hipLaunchKernelGGL(pa::debug_spans, dim3(dims->batch), dim3(64), 0, (hipStream_t)hip_stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "debug_spans launch");
+  return PA_OK;
+}
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG: invalid argument";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: valid request not implemented";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
+    case PA_ERR_HIP: return "PA_ERR_HIP: HIP runtime error";
+  }
+  return "unknown pa_status";
+}
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

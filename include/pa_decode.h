@@ -1,0 +1,196 @@
+/*
+ * pa_decode.h - paged-attention decode on AMD Instinct MI355X (gfx950).
+ *
+ * A few query tokens per sequence attend over a KV cache held in fixed-size
+ * physical blocks that a per-sequence block table names.  The operation
+ * follows the interface of gllm "feat(backend): sliding-window
+ * PagedAttention" (#116), "What changes — Interface":
+ *     PagedAttention(dst, q, kCache, vCache, blockTables, seqLens,
+ *                    queryLens, scale, window)
+ * with its window rule (summary): for window > 0 the token at position p
+ * attends to positions p-window+1 .. p; window == 0 is unlimited causal
+ * attention.  Query heads are grouped onto KV heads by H_q / H_kv (executorch
+ * PR #18759, review of sdpa_decode_splitk: native GQA via H_q // H_kv).
+ * Multi-token queries (aiter PR #2914 "Pa gluon swa mtp opt": sliding-window
+ * MTP decode) are the trailing query_lens[b] positions of the context and
+ * are causal among themselves.  Long contexts are cut into partitions whose
+ * (max logit, exp-sum, partial output) a second kernel merges by
+ * log-sum-exp (executorch PR #18759 "split-K flash-decoding"; aiter PR #2914
+ * workspace buffers max_logits / exp_sums / temporary_output).
+ *
+ * Definition.  For sequence b with context length L_b = seq_lens[b] (the
+ * query tokens included) and q_b = query_lens[b] query tokens, query token
+ * i in [0, q_b) sits at position p = L_b - q_b + i.  Query head h_q uses KV
+ * head h = h_q / G, G = H_q / H_kv.  Its visible positions are
+ * [lo, p] with lo = 0 if window == 0 else max(0, p - window + 1).  With
+ * s_t = scale * <q, k_t>, out = sum_t softmax(s)_t * v_t.
+ *
+ * Memory layouts (row-major, contiguous, all device memory):
+ *   q, out        [T, H_q, D], T = sum_b q_b; sequence b owns rows
+ *                 qoff_b .. qoff_b + q_b - 1, qoff_b = q_0 + ... + q_{b-1}
+ *   k_cache       [num_blocks, H_kv, block_size, D]    (one row per position)
+ *   v_cache       [num_blocks, H_kv, D, block_size]    (one column per position)
+ *   block_tables  int32 [B, max_blocks_per_seq]; position t of sequence b
+ *                 lives in physical block block_tables[b][t / block_size] at
+ *                 slot t % block_size
+ *   seq_lens, query_lens   int32 [B]
+ * q, k_cache, v_cache and out share one element type (pa_dims.dtype).
+ *
+ * Device-side preconditions (not checked on the hot path; violating them is
+ * undefined behaviour):  0 <= q_b <= L_b <= max_seq_len, q_b <= max_query_len,
+ * and block_tables[b][k] in [0, num_blocks) for every k < ceil(L_b/block_size)
+ * that holds a visible position.  Table entries beyond those, cache slots
+ * at or past L_b, and blocks no row can see are never used: they may hold
+ * anything, NaN included.
+ *
+ * Ownership and streams.  The caller owns every buffer, the workspace too;
+ * the library allocates and frees nothing.  Work is enqueued on the given HIP
+ * stream (NULL = the default stream); no call synchronises the host or reads
+ * device memory from the host.  Calls are reentrant; calls that share one
+ * workspace must be ordered on one stream.
+ *
+ * Errors.  No call throws.  Every host-visible argument is validated before
+ * any HIP call; a failing call returns a status and leaves a thread-local
+ * message readable through pa_last_error().
+ */
+#ifndef PA_DECODE_H
+#define PA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad size or shape */
+  PA_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement */
+  PA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
+  PA_ERR_HIP = 4            /* a HIP runtime call failed (message has the HIP error) */
+} pa_status;
+
+typedef enum pa_dtype {
+  PA_F32 = 0,               /* IEEE binary32 */
+  PA_BF16 = 1               /* bfloat16 */
+} pa_dtype;
+
+/* Shapes a raw-pointer interface cannot infer.  All host-side values. */
+typedef struct pa_dims {
+  int32_t batch;              /* B >= 0 */
+  int32_t num_q_heads;        /* H_q, a multiple of num_kv_heads */
+  int32_t head_dim;           /* D: 64 or 128 */
+  int32_t max_query_len;      /* upper bound on query_lens[b], >= 1 */
+  int32_t max_seq_len;        /* upper bound on seq_lens[b], >= 1 */
+  int32_t max_blocks_per_seq; /* row stride of block_tables, >= ceil(max_seq_len/block_size) */
+  int32_t num_blocks;         /* physical blocks in each cache, >= 1 */
+  int32_t dtype;              /* pa_dtype of q, k_cache, v_cache and out */
+} pa_dims;
+
+/* Kernel families for the partition step. */
+typedef enum pa_path {
+  PA_PATH_AUTO = 0,
+  PA_PATH_VALU = 1,           /* vector-ALU dot products; any dtype */
+  PA_PATH_MFMA = 2            /* bf16 matrix cores (16-row tiles); bf16 only */
+} pa_path;
+
+/* Launch plan: a pure function of the arguments below and the CU count. */
+typedef struct pa_plan {
+  int32_t path;               /* PA_PATH_VALU or PA_PATH_MFMA */
+  int32_t rows;               /* R = G * max_query_len rows per KV head */
+  int32_t span_max;           /* longest windowed span over the batch bound */
+  int32_t part_size;          /* positions per partition, a multiple of 32 */
+  int32_t num_parts;          /* partition-grid extent per (sequence, KV head) */
+  int32_t waves;              /* 64-lane waves per partition workgroup */
+  int32_t one_shot;           /* 1: a single partition writes out directly */
+  int32_t reserved;
+  uint64_t workspace_bytes;   /* bytes pa_decode needs in `workspace` (0 if one_shot) */
+} pa_plan;
+
+/* Optional controls for pa_decode_ex / pa_plan_compute (zero = automatic). */
+typedef struct pa_options {
+  int32_t path;               /* pa_path; AUTO picks by dtype and R */
+  int32_t part_size;          /* force the partition size (multiple of 32), 0 = auto */
+  int32_t waves;              /* force waves per workgroup (1, 2 or 4), 0 = auto */
+  int32_t reserved;
+  void* event_begin;          /* hipEvent_t recorded on the stream just before the
+                                 partition kernel, or NULL */
+  void* event_end;            /* hipEvent_t recorded just after it, or NULL */
+} pa_options;
+
+/*
+ * Computes the launch plan without touching a device.  `num_cus` is the
+ * compute-unit count the heuristic sizes the grid for (256 on MI355X).
+ * Returns PA_ERR_INVALID_ARG / PA_ERR_UNSUPPORTED for arguments pa_decode
+ * would reject.  `opts` may be NULL.
+ */
+pa_status pa_plan_compute(const pa_dims* dims, int32_t window, int32_t num_kv_heads,
+                          int32_t block_size, int32_t num_cus, const pa_options* opts,
+                          pa_plan* plan);
+
+/*
+ * Workspace bytes pa_decode needs for these arguments on the current HIP
+ * device (its CU count is read once per device and cached).  0 means no
+ * workspace is needed (one partition per sequence).
+ */
+pa_status pa_decode_workspace_size(const pa_dims* dims, int32_t window, int32_t num_kv_heads,
+                                   int32_t block_size, size_t* bytes);
+pa_status pa_decode_workspace_size_ex(const pa_dims* dims, int32_t window, int32_t num_kv_heads,
+                                      int32_t block_size, const pa_options* opts, size_t* bytes);
+
+/*
+ * Paged-attention decode: writes out[T, H_q, D].
+ *   out, q, k_cache, v_cache   device pointers, 16-byte aligned, layouts above
+ *   block_tables, seq_lens, query_lens   device int32 arrays, 4-byte aligned
+ *   scale      finite logit scale
+ *   window     0 (unlimited causal) or the window length in positions
+ *   workspace  device scratch of at least pa_decode_workspace_size() bytes,
+ *              256-byte aligned; may be NULL when that size is 0
+ *   hip_stream hipStream_t or NULL
+ */
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* seq_lens,
+                    const int32_t* query_lens, float scale, int32_t window,
+                    int32_t num_kv_heads, int32_t block_size, const pa_dims* dims,
+                    void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* pa_decode with explicit plan controls and optional timing events. */
+pa_status pa_decode_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* seq_lens,
+                       const int32_t* query_lens, float scale, int32_t window,
+                       int32_t num_kv_heads, int32_t block_size, const pa_dims* dims,
+                       void* workspace, size_t workspace_bytes, void* hip_stream,
+                       const pa_options* opts);
+
+/*
+ * Index dump for bit-exact checks: runs the device index helpers the
+ * partition kernels use and writes, into device int32 arrays,
+ *   seq_info  [B, 4]   qoff_b, lo_b, hi_b (union of visible ranges [lo_b, hi_b)),
+ *                      number of non-empty partitions of sequence b
+ *   row_info  [T, 2]   per query token: first visible position lo_i and its
+ *                      own position p_i
+ *   blocks    [B, max_blocks_per_seq]   physical block id the kernels read for
+ *                      logical block k, or -1 if no visible position is in it
+ *   parts     [B, num_parts, 2]   [start, end) of each partition (empty: start == end)
+ * for the plan `opts` selects (num_parts from pa_plan_compute).  The kernel
+ * reads only seq_lens, query_lens and table entries that hold visible
+ * positions.
+ */
+pa_status pa_debug_spans(const int32_t* block_tables, const int32_t* seq_lens,
+                         const int32_t* query_lens, int32_t window, int32_t num_kv_heads,
+                         int32_t block_size, const pa_dims* dims, const pa_options* opts,
+                         int32_t* seq_info, int32_t* row_info, int32_t* blocks,
+                         int32_t* parts, void* hip_stream);
+
+/* Static description of a status code. */
+const char* pa_status_string(pa_status status);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_DECODE_H */

@@ -1,0 +1,87 @@
+"""Helpers for GPU parity tests: run the HIP path, and hand the oracle a
+compact host copy of exactly the blocks it needs (data movement only)."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import decode_attention_pa_amd as pa
+from oracle import paged_attention as ref
+
+BF16_TOL = 2e-2   # max-abs bar for bf16 inputs with fp32 accumulation
+F32_TOL = 1e-4    # max-abs bar for fp32 inputs
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(case, out=None, **opts):
+    """One pa_decode call on the case's tensors; returns the output tensor."""
+    if out is None:
+        out = case.new_out().fill_(float("nan"))
+    pa.decode(out, case.q, case.k_cache, case.v_cache, case.block_tables, case.seq_lens,
+              case.query_lens, case.scale, case.window, case.w.num_kv_heads, case.w.block_size,
+              max_seq_len=case.w.max_seq_len, max_query_len=max(case.w.query_len,
+                                                                   max(case.query_lens_host or [1])),
+              **opts)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_inputs(case, seqs=None):
+    """Compact oracle problem for sequences ``seqs`` (default all).
+
+    Gathers only blocks that hold visible positions; table entries for other
+    logical blocks point at a NaN block, so a wrong read would show.
+    Returns (inputs dict, list of global q rows in compact order).
+    """
+    B = len(case.seq_lens_host)
+    seqs = list(range(B)) if seqs is None else list(seqs)
+    tables = case.tables_host.numpy()
+    sp = ref.spans(tables, case.seq_lens_host, case.query_lens_host, case.window,
+                   case.w.block_size)
+    need = sorted(set(int(x) for b in seqs for x in sp[b]["blocks"] if x >= 0))
+    remap = {p: i + 1 for i, p in enumerate(need)}
+    ids = torch.tensor(need, dtype=torch.long, device=case.k_cache.device)
+    k = case.k_cache.index_select(0, ids).float().cpu().numpy() if need else \
+        np.zeros((0,) + tuple(case.k_cache.shape[1:]), np.float32)
+    v = case.v_cache.index_select(0, ids).float().cpu().numpy() if need else \
+        np.zeros((0,) + tuple(case.v_cache.shape[1:]), np.float32)
+    k = np.concatenate([np.full((1,) + k.shape[1:], np.nan, np.float32), k])
+    v = np.concatenate([np.full((1,) + v.shape[1:], np.nan, np.float32), v])
+    ctab = np.zeros((len(seqs), tables.shape[1]), np.int64)
+    rows = []
+    for r, b in enumerate(seqs):
+        for kk, p in enumerate(sp[b]["blocks"]):
+            ctab[r, kk] = remap[int(p)] if p >= 0 else 0
+        rows.extend(range(sp[b]["qoff"], sp[b]["qoff"] + case.query_lens_host[b]))
+    qh = case.q.float().cpu().numpy()[rows] if rows else np.zeros((0,) + tuple(case.q.shape[1:]))
+    return dict(q=qh, k_cache=k, v_cache=v, block_tables=ctab,
+                seq_lens=np.array([case.seq_lens_host[b] for b in seqs]),
+                query_lens=np.array([case.query_lens_host[b] for b in seqs]),
+                scale=case.scale, window=case.window, num_kv_heads=case.w.num_kv_heads,
+                block_size=case.w.block_size), rows
+
+
+def oracle_out(case, seqs=None):
+    inp, rows = oracle_inputs(case, seqs)
+    return ref.decode(**inp), rows
+
+
+def compare(out_gpu, expect, rows, tol, label=""):
+    got = out_gpu.float().cpu().numpy()[rows].astype(np.float64)
+    assert got.shape == expect.shape
+    assert np.all(np.isfinite(got)), f"{label}: non-finite GPU output"
+    err = np.abs(got - expect)
+    mx = float(err.max()) if err.size else 0.0
+    scale = float(np.abs(expect).max()) if expect.size else 0.0
+    rms_ratio = float(np.sqrt((err ** 2).mean() / max((expect ** 2).mean(), 1e-300))) if err.size else 0.0
+    say(f"[parity] {label}: max_abs={mx:.3e} max|ref|={scale:.3e} rel={mx / max(scale, 1e-30):.3e} "
+        f"rms_ratio={rms_ratio:.3e} tol={tol:g}")
+    assert mx <= tol, f"{label}: max-abs {mx:.3e} > {tol:g}"
+    return mx, rms_ratio

@@ -1,0 +1,190 @@
+"""CPU tests of the C-ABI library: it loads, exports every declared symbol,
+and its host logic (argument validation, launch plan, workspace size) behaves
+as documented in include/pa_decode.h.  No call here touches a GPU."""
+
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import decode_attention_pa_amd as pa
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa_decode.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pa.library_path()):
+        pytest.fail("libpa_decode.so is not built (run python -m decode_attention_pa_amd.build)")
+    return pa.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert declared_functions() == sorted(pa.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", pa.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert lib.pa_status_string(code).decode().startswith("PA_")
+    assert b"unknown" in lib.pa_status_string(99)
+
+
+def dims_of(w: workloads.Workload, max_query_len=None, **over):
+    d = dict(batch=w.batch, num_q_heads=w.num_q_heads, head_dim=w.head_dim,
+             max_query_len=w.query_len if max_query_len is None else max_query_len, max_seq_len=w.max_seq_len,
+             max_blocks_per_seq=w.max_blocks_per_seq, num_blocks=1000,
+             dtype=pa.F32 if w.dtype == "f32" else pa.BF16)
+    d.update(over)
+    return pa.make_dims(**d)
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_plan_covers_longest_span(lib, name):
+    w = workloads.WORKLOADS[name]
+    for win in w.windows:
+        p = pa.plan(dims_of(w), win, w.num_kv_heads, w.block_size, num_cus=256)
+        G = w.num_q_heads // w.num_kv_heads
+        assert p["rows"] == G * w.query_len
+        span = w.max_seq_len if win == 0 else min(w.max_seq_len, win + w.query_len - 1)
+        assert p["span_max"] == span
+        assert p["part_size"] % 32 == 0
+        # every sequence's chunk-aligned span fits in the partition grid
+        assert p["num_parts"] * p["part_size"] >= span + 31
+        assert p["one_shot"] == (p["num_parts"] == 1)
+        if p["one_shot"]:
+            assert p["workspace_bytes"] == 0
+        else:
+            states = w.batch * w.num_kv_heads * p["num_parts"] * p["rows"]
+            al = lambda x: (x + 255) // 256 * 256
+            assert p["workspace_bytes"] == 2 * al(4 * states) + al(4 * states * w.head_dim)
+        expect_path = pa.PATH_VALU if w.dtype == "f32" else pa.PATH_MFMA
+        assert p["path"] == expect_path
+
+
+def test_plan_forced_partition_size(lib):
+    w = workloads.WORKLOADS["long_splitk_bf16"]
+    p = pa.plan(dims_of(w), 0, 1, 16, part_size=4096)
+    assert p["part_size"] == 4096 and p["num_parts"] == math.ceil((131072 + 31) / 4096)
+    p1 = pa.plan(dims_of(w), 0, 1, 16, part_size=1 << 20)
+    assert p1["num_parts"] == 1 and p1["one_shot"] == 1 and p1["workspace_bytes"] == 0
+
+
+def test_plan_uses_more_partitions_on_more_cus(lib):
+    w = workloads.WORKLOADS["long_splitk_bf16"]
+    small = pa.plan(dims_of(w), 0, 1, 16, num_cus=64)
+    big = pa.plan(dims_of(w), 0, 1, 16, num_cus=256)
+    assert big["num_parts"] >= small["num_parts"]
+
+
+def test_plan_window_bounds_the_span(lib):
+    w = workloads.WORKLOADS["large_block_mtp_bf16"]
+    p4096 = pa.plan(dims_of(w), 4096, 8, 1024)
+    p0 = pa.plan(dims_of(w), 0, 8, 1024)
+    assert p4096["span_max"] == 4097 and p0["span_max"] == 65536
+    assert p4096["num_parts"] < p0["num_parts"]
+
+
+BAD = [
+    (dict(head_dim=96), pa.ERR_UNSUPPORTED),
+    (dict(head_dim=0), pa.ERR_UNSUPPORTED),
+    (dict(dtype=7), pa.ERR_INVALID_ARG),
+    (dict(batch=-1), pa.ERR_INVALID_ARG),
+    (dict(num_q_heads=6), pa.ERR_INVALID_ARG),          # not a multiple of 4 KV heads
+    (dict(max_query_len=0), pa.ERR_INVALID_ARG),
+    (dict(max_seq_len=0), pa.ERR_INVALID_ARG),
+    (dict(max_blocks_per_seq=3), pa.ERR_INVALID_ARG),   # 8192 / 16 needs 512
+    (dict(num_blocks=0), pa.ERR_INVALID_ARG),
+    (dict(max_query_len=17), pa.ERR_UNSUPPORTED),       # 4 * 17 rows > 64
+]
+
+
+@pytest.mark.parametrize("over,code", BAD)
+def test_plan_rejects_bad_dims(lib, over, code):
+    w = workloads.WORKLOADS["gqa_bf16"]
+    with pytest.raises(pa.PaError) as e:
+        pa.plan(dims_of(w, **over), 0, 8 if "num_q_heads" not in over else 4, 16)
+    assert e.value.status == code
+    assert lib.pa_last_error().decode()
+
+
+@pytest.mark.parametrize("bs,code", [(8, pa.ERR_UNSUPPORTED), (24, pa.ERR_UNSUPPORTED),
+                                     (2048, pa.ERR_UNSUPPORTED), (0, pa.ERR_UNSUPPORTED)])
+def test_plan_rejects_block_sizes(lib, bs, code):
+    w = workloads.WORKLOADS["gqa_bf16"]
+    with pytest.raises(pa.PaError) as e:
+        pa.plan(dims_of(w, max_blocks_per_seq=100000), 0, 8, bs)
+    assert e.value.status == code
+
+
+def test_plan_rejects_negative_window_and_bad_options(lib):
+    w = workloads.WORKLOADS["gqa_bf16"]
+    for kw, win in [({}, -1), (dict(part_size=48), 0), (dict(part_size=-32), 0),
+                    (dict(waves=3), 0), (dict(path=9), 0)]:
+        with pytest.raises(pa.PaError) as e:
+            pa.plan(dims_of(w), win, 8, 16, **kw)
+        assert e.value.status == pa.ERR_INVALID_ARG
+
+
+def test_plan_rejects_mfma_for_fp32(lib):
+    w = workloads.WORKLOADS["tiny_f32"]
+    with pytest.raises(pa.PaError) as e:
+        pa.plan(dims_of(w), 0, 1, 16, path=pa.PATH_MFMA)
+    assert e.value.status == pa.ERR_UNSUPPORTED
+
+
+def test_decode_validates_before_touching_a_device(lib):
+    """Invalid host arguments fail with a status before any HIP call, so this
+    runs without a GPU."""
+    w = workloads.WORKLOADS["gqa_bf16"]
+    d = dims_of(w)
+    P = ctypes.c_void_p
+    good = P(4096)
+    args = [good] * 7
+    # (the pointers are fake: every call below must fail validation, so no
+    # kernel is ever launched with them, on a machine with or without a GPU)
+    st = lib.pa_decode(None, *args[1:7], ctypes.c_float(0.1), 0, 8, 16, ctypes.byref(d), None, 0, None)
+    assert st == pa.ERR_INVALID_ARG
+    st = lib.pa_decode(P(4097), *args[1:7], ctypes.c_float(0.1), 0, 8, 16, ctypes.byref(d), None, 0, None)
+    assert st == pa.ERR_INVALID_ARG and b"aligned" in lib.pa_last_error()
+    st = lib.pa_decode(*args[:7], ctypes.c_float(float("nan")), 0, 8, 16, ctypes.byref(d), None, 0, None)
+    assert st == pa.ERR_INVALID_ARG and b"scale" in lib.pa_last_error()
+    st = lib.pa_decode(*args[:7], ctypes.c_float(0.1), -2, 8, 16, ctypes.byref(d), None, 0, None)
+    assert st == pa.ERR_INVALID_ARG
+    st = lib.pa_decode(*args[:7], ctypes.c_float(0.1), 0, 8, 16, None, None, 0, None)
+    assert st == pa.ERR_INVALID_ARG
+
+
+def test_empty_batch_is_a_no_op(lib):
+    w = workloads.WORKLOADS["gqa_bf16"]
+    d = dims_of(w, batch=0)
+    P = ctypes.c_void_p
+    st = lib.pa_decode(*([P(4096)] * 7), ctypes.c_float(0.1), 0, 8, 16, ctypes.byref(d), None, 0, None)
+    assert st == pa.OK
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    c = workloads.make_case("tiny_f32", device="cpu")
+    with pytest.raises(pa.PaError):
+        pa.decode(c.new_out(), c.q, c.k_cache, c.v_cache, c.block_tables, c.seq_lens,
+                  c.query_lens, c.scale, 0, 1, 16, max_seq_len=50)

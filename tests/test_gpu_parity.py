@@ -1,0 +1,210 @@
+"""GPU parity: the HIP path against the float64 oracle, element by element.
+
+Small shapes (several 32-position chunks, ragged tails, shuffled blocks, GQA,
+MTP, windows, forced partition sizes, both kernel families) are compared in
+full; the full-size workloads are compared on sampled sequences, in the
+launch configuration the bench times.  Tolerances: max-abs 2e-2 for bf16
+inputs (fp32 accumulation), 1e-4 for fp32 inputs.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_pa_amd as pa
+import workloads
+from oracle import paged_attention as ref
+from tests._gpu_util import BF16_TOL, F32_TOL, compare, oracle_out, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+
+
+def small(seed, dtype="bf16", **over):
+    r = np.random.default_rng(seed)
+    D = int(r.choice([64, 128]))
+    hkv = int(r.choice([1, 2, 3]))
+    G = int(r.choice([1, 2, 4, 8]))
+    ql = int(r.choice([1, 2, 3, 4]))
+    while G * ql > 64:
+        ql -= 1
+    bs = int(r.choice([16, 32, 64, 256]))
+    B = int(r.integers(1, 5))
+    lens = tuple(int(x) for x in r.integers(ql, 700, size=B))
+    mx = max(lens)
+    kw = dict(name=f"small{seed}", dtype=dtype, batch=B, num_q_heads=G * hkv, num_kv_heads=hkv,
+              head_dim=D, block_size=bs, query_len=ql, seq_lens=lens, max_seq_len=mx,
+              max_blocks_per_seq=-(-mx // bs) + 1, pool=0, seed=1000 + seed,
+              scale=float(1.0 / np.sqrt(D)), windows=(0,))
+    kw.update(over)
+    return workloads.custom(**kw)
+
+
+@pytest.mark.parametrize("window", [0, 5])
+def test_tiny_f32(window):
+    c = workloads.make_case("tiny_f32", device="cuda", window=window)
+    say(f"[case] tiny_f32 window={window}")
+    exp, rows = oracle_out(c)
+    compare(run_gpu(c), exp, rows, F32_TOL, f"tiny_f32 w={window}")
+    for P in (32, 64):
+        compare(run_gpu(c, part_size=P), exp, rows, F32_TOL, f"tiny_f32 w={window} P={P}")
+
+
+@pytest.mark.parametrize("path", [pa.PATH_MFMA, pa.PATH_VALU])
+@pytest.mark.parametrize("seed", range(10))
+def test_small_bf16(seed, path):
+    w = small(seed)
+    for win in (0, 1, 5, 37, 100000):
+        c = workloads.make_case(w, device="cuda", window=win)
+        say(f"[case] small seed={seed} path={path} window={win} {w}")
+        exp, rows = oracle_out(c)
+        for P in (0, 32, 64):
+            compare(run_gpu(c, path=path, part_size=P), exp, rows, BF16_TOL,
+                    f"small{seed} path={path} w={win} P={P}")
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_small_f32(seed):
+    w = small(seed + 40, dtype="f32")
+    for win in (0, 3, 64):
+        c = workloads.make_case(w, device="cuda", window=win)
+        say(f"[case] small f32 seed={seed} window={win}")
+        exp, rows = oracle_out(c)
+        for P in (0, 32, 96):
+            compare(run_gpu(c, part_size=P), exp, rows, F32_TOL, f"small-f32 {seed} w={win} P={P}")
+
+
+@pytest.mark.parametrize("waves", [1, 2, 4])
+def test_mfma_waves(waves):
+    w = small(7, head_dim=128, num_q_heads=8, num_kv_heads=2, query_len=2)  # R = 8: one row tile
+    c = workloads.make_case(w, device="cuda", window=0)
+    exp, rows = oracle_out(c)
+    for P in (32, 96, 256):
+        compare(run_gpu(c, path=pa.PATH_MFMA, waves=waves, part_size=P), exp, rows, BF16_TOL,
+                f"waves={waves} P={P}")
+
+
+def test_max_rows_and_edge_lengths():
+    """R = 64 (4 row tiles), contexts of 1, q == L, lengths at chunk edges, and
+    sequences with no query tokens."""
+    lens = (1, 4, 31, 32, 33, 64, 65, 700)
+    qls = (1, 4, 4, 0, 2, 4, 0, 3)
+    for D in (64, 128):
+        w = small(3, head_dim=D, num_q_heads=16, num_kv_heads=1, query_len=4, batch=len(lens),
+                  seq_lens=lens, query_lens=qls, block_size=32, max_seq_len=700,
+                  max_blocks_per_seq=23)
+        for win in (0, 2, 40):
+            c = workloads.make_case(w, device="cuda", window=win)
+            exp, rows = oracle_out(c)
+            for path in (pa.PATH_MFMA, pa.PATH_VALU):
+                for P in (0, 32):
+                    compare(run_gpu(c, path=path, part_size=P), exp, rows, BF16_TOL,
+                            f"edges D={D} w={win} path={path} P={P}")
+
+
+def test_debug_spans_bit_exact():
+    for name in workloads.WORKLOADS:
+        w = workloads.WORKLOADS[name]
+        for win in w.windows:
+            c = workloads.make_case(w, device="cuda", window=win, poison=False) if name in (
+                "tiny_f32",) else _tables_only(w, win)
+            _check_spans(c, win)
+    for seed in range(6):
+        w = small(seed)
+        for win in (0, 1, 5, 37):
+            _check_spans(workloads.make_case(w, device="cuda", window=win), win)
+
+
+class _TablesOnly:
+    pass
+
+
+def _tables_only(w, win):
+    """Lengths and tables of a workload without materialising its KV pool."""
+    import math
+    g = torch.Generator().manual_seed(w.seed)
+    lens, qls = workloads._lengths(w, g)
+    c = _TablesOnly()
+    c.w = w
+    c.window = win
+    c.seq_lens_host, c.query_lens_host = lens, qls
+    bs = w.block_size
+    nblk = [-(-L // bs) for L in lens]
+    pool = w.pool or math.ceil(1.25 * sum(nblk))
+    perm = torch.randperm(max(pool, sum(nblk) + 1), generator=g).tolist()
+    t = torch.full((w.batch, w.max_blocks_per_seq), perm[sum(nblk)], dtype=torch.int32)
+    off = 0
+    for b, n in enumerate(nblk):
+        t[b, :n] = torch.tensor(perm[off:off + n], dtype=torch.int32)
+        off += n
+    c.tables_host = t
+    c.block_tables = t.cuda()
+    c.seq_lens = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    c.query_lens = torch.tensor(qls, dtype=torch.int32, device="cuda")
+    c.num_blocks = pool
+    return c
+
+
+def _check_spans(c, win):
+    w = c.w
+    dims = pa.make_dims(w.batch, w.num_q_heads, w.head_dim, max(w.query_len, max(c.query_lens_host)),
+                        w.max_seq_len, w.max_blocks_per_seq, c.num_blocks,
+                        pa.F32 if w.dtype == "f32" else pa.BF16)
+    T = sum(c.query_lens_host)
+    got = pa.debug_spans(c.block_tables, c.seq_lens, c.query_lens, win, w.num_kv_heads,
+                         w.block_size, dims, T)
+    torch.cuda.synchronize()
+    sp = ref.spans(c.tables_host.numpy(), c.seq_lens_host, c.query_lens_host, win, w.block_size)
+    si = got["seq_info"].cpu().numpy()
+    ri = got["row_info"].cpu().numpy()
+    bl = got["blocks"].cpu().numpy()
+    parts = got["parts"].cpu().numpy()
+    P = got["plan"]["part_size"]
+    for b, s in enumerate(sp):
+        assert si[b, 0] == s["qoff"], (w.name, b)
+        if c.query_lens_host[b] > 0:
+            assert (si[b, 1], si[b, 2]) == (s["lo"], s["hi"]), (w.name, b)
+            np.testing.assert_array_equal(bl[b], s["blocks"])
+            for i, (lo_i, p_i) in enumerate(s["rows"]):
+                assert tuple(ri[s["qoff"] + i]) == (lo_i, p_i)
+            # partitions tile [lo, hi) exactly, in order, none longer than P
+            n = si[b, 3]
+            assert n >= 1
+            pr = parts[b, :n]
+            assert pr[0, 0] == s["lo"] and pr[-1, 1] == s["hi"]
+            assert np.all(pr[1:, 0] == pr[:-1, 1])
+            assert np.all(pr[:, 1] > pr[:, 0]) and np.all(pr[:, 1] - pr[:, 0] <= P)
+            assert np.all(parts[b, n:, 0] == parts[b, n:, 1])
+        else:
+            assert si[b, 3] == 0 and np.all(bl[b] == -1)
+    say(f"[spans] {w.name} w={win}: bit-exact")
+
+
+FULL = [("gqa_bf16", 0, None), ("swa_mtp_bf16", 128, None), ("long_splitk_bf16", 0, None),
+        ("large_block_mtp_bf16", 4096, 24), ("large_block_mtp_bf16", 0, 2)]
+
+
+@pytest.mark.parametrize("name,window,nsample", FULL)
+def test_full_workload(name, window, nsample):
+    w = workloads.WORKLOADS[name]
+    say(f"[case] full {name} window={window}")
+    c = workloads.make_case(w, device="cuda", window=window)
+    out = run_gpu(c)
+    B = w.batch
+    if nsample is None:
+        seqs = list(range(B))
+    else:
+        lens = np.array(c.seq_lens_host)
+        r = np.random.default_rng(w.seed)
+        pick = set([int(lens.argmax()), int(lens.argmin())])
+        pick |= set(int(x) for x in r.choice(B, size=nsample, replace=False))
+        seqs = sorted(pick)[:max(nsample, 2)]
+    exp, rows = oracle_out(c, seqs)
+    compare(out, exp, rows, BF16_TOL, f"{name} w={window} seqs={len(seqs)}")
+    # rows not compared must still be finite and written
+    assert torch.isfinite(out.float()).all()
