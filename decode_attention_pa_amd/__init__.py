@@ -269,6 +269,7 @@ class Prepared:
                   block_size)
         self.dims = dims_for(q, k_cache, block_tables, max_query_len, max_seq_len)
         self.opts = make_options(path, part_size, waves, event_begin, event_end)
+        self._events = (event_begin, event_end)
         self.plan = plan(self.dims, window, num_kv_heads, block_size,
                          num_cus=torch.cuda.get_device_properties(q.device).multi_processor_count,
                          path=path, part_size=part_size, waves=waves)
@@ -290,6 +291,10 @@ class Prepared:
         self._fn = load().pa_decode_ex
 
     def set_events(self, event_begin, event_end):
+        """Events the library records around the partition kernel on every
+        later call (None to stop).  The objects are kept alive here, since
+        the library records into them until they are replaced."""
+        self._events = (event_begin, event_end)
         self.opts.event_begin = _event_handle(event_begin)
         self.opts.event_end = _event_handle(event_end)
 

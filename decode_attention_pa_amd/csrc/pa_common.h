@@ -103,7 +103,28 @@ struct PartArgs {
   int part_size;               // P, multiple of kChunk * waves
   int log2_bs;
   int max_blocks_per_seq;
+  int batch;
 };
+
+// Work-item of a partition workgroup.  The grid is 1-D and ordered with the
+// KV head fastest and the partition slowest: workgroups are handed to the 8
+// XCDs round-robin by id, so consecutive ids must carry comparable work.
+// (With the partition fastest and 8 partitions per sequence, partition j
+// would always land on XCD j, and high partitions exist only for long
+// sequences.)
+struct PartItem {
+  int j, h, b;
+};
+
+__device__ inline PartItem part_item(const PartArgs& a) {
+  const int id = blockIdx.x;
+  PartItem it;
+  it.h = id % a.num_kv_heads;
+  const int r = id / a.num_kv_heads;
+  it.b = r % a.batch;
+  it.j = r / a.batch;
+  return it;
+}
 
 struct ReduceArgs {
   void* out;

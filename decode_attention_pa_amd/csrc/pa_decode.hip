@@ -130,16 +130,17 @@ pa_status make_plan(const pa_dims* d, int32_t window, int32_t hkv, int32_t bs, i
                   pa::kChunk);
     r.part_size = p_req;
   } else {
-    // Enough partitions for ~ 2 workgroups per CU when every (sequence, KV
-    // head) has the longest span; partitions of at least 8 chunks so the
-    // partial-state traffic stays small, at most 64 chunks so that unequal
-    // sequence lengths do not leave a long tail.
+    // Enough partitions for ~8 workgroups per CU if every (sequence, KV
+    // head) had the longest span (real batches average less), with
+    // partitions of 8..128 chunks: longer ones amortise each workgroup's
+    // set-up and keep the partial states small, shorter ones would
+    // multiply the LSE merge's work.  Constants measured on MI355X.
     const int64_t units = (int64_t)d->batch * hkv;
     const int64_t chunks = cdiv(span_cover, pa::kChunk);
-    const int64_t want = std::max<int64_t>(1, cdiv(2 * (int64_t)num_cus, std::max<int64_t>(units, 1)));
+    const int64_t want = std::max<int64_t>(1, cdiv(8 * (int64_t)num_cus, std::max<int64_t>(units, 1)));
     int64_t pc = cdiv(chunks, want);
     pc = std::max<int64_t>(pc, 8);
-    pc = std::min<int64_t>(pc, 64);
+    pc = std::min<int64_t>(pc, 128);
     r.part_size = (int32_t)(pc * pa::kChunk);
   }
   r.num_parts = (int32_t)std::max<int64_t>(1, cdiv(span_cover, r.part_size));
@@ -249,6 +250,7 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
   a.part_size = p.part_size;
   a.log2_bs = ilog2_exact(bs);
   a.max_blocks_per_seq = d->max_blocks_per_seq;
+  a.batch = d->batch;
 
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
@@ -256,7 +258,9 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
     e = hipEventRecord((hipEvent_t)o->event_begin, s);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord(begin)");
   }
-  const dim3 grid(p.num_parts, hkv, d->batch);
+  const uint64_t nwg = (uint64_t)p.num_parts * hkv * d->batch;
+  if (nwg > 0x7fffffffull) return fail(PA_ERR_UNSUPPORTED, "grid of %llu workgroups too large", (unsigned long long)nwg);
+  const dim3 grid((uint32_t)nwg);
   const int nrt = (p.rows + 15) / 16;
   bool ok = true;
   if (p.path == PA_PATH_MFMA) {
@@ -291,14 +295,18 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
     r.rows = p.rows;
     r.num_parts = p.num_parts;
     r.part_size = p.part_size;
-    const dim3 rgrid(p.rows, hkv, d->batch);
+    const bool narrow = p.num_parts <= pa::kNarrowMaxParts;
+    const dim3 rgrid = narrow ? dim3(hkv, d->batch)
+                              : dim3(p.rows * (d->head_dim / pa::kReduceSlice), hkv, d->batch);
+#define PA_REDUCE(T, D)                                                                      \
+  if (narrow) hipLaunchKernelGGL((pa::lse_reduce_narrow<T, D>), rgrid, dim3(256), 0, s, r); \
+  else hipLaunchKernelGGL((pa::lse_reduce_wide<T, D>), rgrid, dim3(256), 0, s, r);
     if (d->dtype == PA_F32) {
-      if (d->head_dim == 64) hipLaunchKernelGGL((pa::lse_reduce<float, 64>), rgrid, dim3(256), 0, s, r);
-      else hipLaunchKernelGGL((pa::lse_reduce<float, 128>), rgrid, dim3(256), 0, s, r);
+      if (d->head_dim == 64) { PA_REDUCE(float, 64) } else { PA_REDUCE(float, 128) }
     } else {
-      if (d->head_dim == 64) hipLaunchKernelGGL((pa::lse_reduce<uint16_t, 64>), rgrid, dim3(256), 0, s, r);
-      else hipLaunchKernelGGL((pa::lse_reduce<uint16_t, 128>), rgrid, dim3(256), 0, s, r);
+      if (d->head_dim == 64) { PA_REDUCE(uint16_t, 64) } else { PA_REDUCE(uint16_t, 128) }
     }
+#undef PA_REDUCE
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "reduce kernel launch");
   }

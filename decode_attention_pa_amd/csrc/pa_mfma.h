@@ -33,20 +33,35 @@
 
 namespace pa {
 
-template <int D>
-struct MfmaChunk {
-  u32x4 k[2][D / 32];  // K: [tile][k-step], 8 bf16 of one position each
-  u32x4 v[D / 16];     // V^T: [dim tile], 8 consecutive positions of one dim
-};
-
 __device__ inline bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+// 16-byte load of streamed KV data (read once per call).
+__device__ inline u32x4 ld_stream(const uint16_t* p) {
+#ifdef PA_NT_LOADS
+  return __builtin_nontemporal_load((const u32x4*)p);
+#else
+  return *(const u32x4*)p;
+#endif
+}
+
+// Physical blocks touched by one chunk: the chunk's in-partition positions
+// [lo, hi] span at most two blocks (block_size >= 16 >= chunk / 2).  The ids
+// are wave-uniform, so they come through the scalar cache (their own wait
+// counter: no false dependence on the vector loads in flight).
+struct ChunkBlocks {
+  int first_idx;  // logical block index of the first in-partition position
+  int first;      // its physical block
+  int second;     // physical block of the last in-partition position
+};
 
 template <int D, int NRT, int NW>
 __global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
-  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const PartItem it = part_item(a);
+  const int j = it.j, h = it.h, b = it.b;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ln = lane & 15, lg = lane >> 4;
 
   const int L = a.seq_lens[b];
@@ -93,24 +108,43 @@ __global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
     }
   }
 
-  auto load = [&](int k, MfmaChunk<D>& r) {
+  auto blocks_of = [&](int k) {
+    const int cs = cb0 + k * kChunk;
+    const int lo = max(cs, ps);
+    const int hi = min(cs + kChunk - 1, pe - 1);
+    ChunkBlocks cb;
+    cb.first_idx = __builtin_amdgcn_readfirstlane(lo >> log2_bs);
+    const int second_idx = __builtin_amdgcn_readfirstlane(hi >> log2_bs);
+    cb.first = __builtin_amdgcn_readfirstlane(table[cb.first_idx]);
+    cb.second = __builtin_amdgcn_readfirstlane(table[second_idx]);
+    return cb;
+  };
+  // K rows: lane (ln, lg) of tile t holds position 8*(ln/4) + 4*t + ln%4 of
+  // the chunk, dims 8*lg + 32*s .. +7 for k-step s.
+  auto load_k = [&](int k, const ChunkBlocks& cb, u32x4 (&kr)[2][KS]) {
     const int cs = cb0 + k * kChunk;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       int pos = cs + 8 * (ln >> 2) + 4 * t + (ln & 3);
       pos = min(max(pos, ps), pe - 1);  // clamp: never touch blocks outside the span
-      const int blk = phys_block(table, pos, log2_bs);
-      const uint16_t* kp = kc + (size_t)blk * blk_stride + head_off + (size_t)(pos & bs_mask) * D;
+      const int blk = (pos >> log2_bs) == cb.first_idx ? cb.first : cb.second;
+      const uint16_t* kp =
+          kc + (size_t)blk * blk_stride + head_off + (size_t)(pos & bs_mask) * D + lg * 8;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) r.k[t][s] = *(const u32x4*)(kp + (4 * s + lg) * 8);
+      for (int s = 0; s < KS; ++s) kr[t][s] = ld_stream(kp + s * 32);
     }
+  };
+  // V^T columns: lane (ln, lg) holds dim 16*dt + ln, positions 8*lg .. +7.
+  auto load_v = [&](int k, const ChunkBlocks& cb, u32x4 (&vr)[DT]) {
+    const int cs = cb0 + k * kChunk;
     int p8 = cs + 8 * lg;
-    if (p8 + 8 <= ps || p8 >= pe) p8 = ps & ~7;  // wholly outside: read a valid group, zeroed later
-    const int vblk = phys_block(table, p8, log2_bs);
-    const uint16_t* vp = vc + (size_t)vblk * blk_stride + head_off + (p8 & bs_mask);
+    if (p8 + 8 <= ps || p8 >= pe) p8 = max(cs, ps) & ~7;  // wholly outside: any valid group, zeroed later
+    else p8 = max(p8, ps & ~7);
+    const int blk = (p8 >> log2_bs) == cb.first_idx ? cb.first : cb.second;
+    const uint16_t* vp = vc + (size_t)blk * blk_stride + head_off + (p8 & bs_mask) +
+                         ((size_t)ln << log2_bs);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      r.v[dt] = *(const u32x4*)(vp + ((size_t)(16 * dt + ln) << log2_bs));
+    for (int dt = 0; dt < DT; ++dt) vr[dt] = ld_stream(vp + ((size_t)(16 * dt) << log2_bs));
   };
 
   f32x4 o[NRT][DT];
@@ -124,33 +158,33 @@ __global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
   }
   const float scale_log2 = a.scale_log2;
 
-  auto compute = [&](int k, const MfmaChunk<D>& r) {
+  // Software pipeline, one chunk deep: the next chunk's K rows are requested
+  // as soon as QK has consumed the current ones, its V columns as soon as PV
+  // has; block ids run two chunks ahead through the scalar cache.  Loads are
+  // issued unconditionally (the last iteration re-requests its own chunk, a
+  // cache hit) so that the wait counts are the same on every path.
+  int k = wave;
+  u32x4 kr[2][KS], vr[DT];
+  ChunkBlocks nb = {0, 0, 0};
+  if (k < nck) {
+    const ChunkBlocks cb = blocks_of(k);
+    load_k(k, cb, kr);
+    load_v(k, cb, vr);
+    nb = blocks_of(min(k + NW, nck - 1));
+  }
+  for (; k < nck; k += NW) {
+    const int kn = min(k + NW, nck - 1);
     const int cs = cb0 + k * kChunk;
     const int p8 = cs + 8 * lg;
-    u32x4 vv[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) vv[dt] = r.v[dt];
-    if (cs < ps || cs + kChunk > pe) {
-      // Edge chunk: zero V entries of positions outside [ps, pe) so that a
-      // zero weight never meets a stale (possibly NaN) value.
-      u32x4 keep;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int t0 = p8 + 2 * w;
-        const uint32_t lo16 = (t0 >= ps && t0 < pe) ? 0x0000ffffu : 0u;
-        const uint32_t hi16 = (t0 + 1 >= ps && t0 + 1 < pe) ? 0xffff0000u : 0u;
-        keep[w] = lo16 | hi16;
-      }
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) vv[dt] &= keep;
-    }
+    bf16x8 pb[NRT];
+    float alpha[NRT];
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
       f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.k[0][s]), qf[rt][s], sa, 0, 0, 0);
-        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.k[1][s]), qf[rt][s], sb, 0, 0, 0);
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[0][s]), qf[rt][s], sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[1][s]), qf[rt][s], sb, 0, 0, 0);
       }
       float x[8];
 #pragma unroll
@@ -165,36 +199,44 @@ __global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float mnew = fmaxf(mrun[rt], mx);
       const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f(mrun[rt] - mref);
+      alpha[rt] = __builtin_amdgcn_exp2f(mrun[rt] - mref);
       mrun[rt] = mnew;
-      bf16x8 pb;
       float psum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const __bf16 pe16 = (__bf16)__builtin_amdgcn_exp2f(x[e] - mref);
-        pb[e] = pe16;
+        pb[rt][e] = pe16;
         psum += (float)pe16;  // normalise by the weights PV actually applies
       }
-      lrun[rt] = lrun[rt] * alpha + psum;
+      lrun[rt] = lrun[rt] * alpha[rt] + psum;
+    }
+    load_k(kn, nb, kr);
+    const ChunkBlocks nb2 = blocks_of(min(k + 2 * NW, nck - 1));
+    // Keep V-dependent work below this point: the V columns are the last
+    // loads to arrive, and waiting for them earlier would serialise the
+    // next chunk's K requests behind them.
+    __builtin_amdgcn_sched_barrier(0);
+    // Zero V entries of positions outside [ps, pe) (only edge chunks have
+    // any) so that a zero weight never meets a stale, possibly NaN, value.
+    u32x4 keep;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int t0 = p8 + 2 * w;
+      const uint32_t lo16 = (t0 >= ps && t0 < pe) ? 0x0000ffffu : 0u;
+      const uint32_t hi16 = (t0 + 1 >= ps && t0 + 1 < pe) ? 0xffff0000u : 0u;
+      keep[w] = lo16 | hi16;
+    }
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        o[rt][dt] *= alpha;
-        o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vv[dt]), pb, o[rt][dt], 0, 0, 0);
+        o[rt][dt] *= alpha[rt];
+        o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vr[dt] & keep), pb[rt],
+                                                            o[rt][dt], 0, 0, 0);
       }
     }
-  };
-
-  {
-    MfmaChunk<D> cur, nxt;
-    int k = wave;
-    if (k < nck) load(k, cur);
-    while (k < nck) {
-      const int kn = k + NW;
-      if (kn < nck) load(kn, nxt);  // keep the next chunk's loads in flight
-      compute(k, cur);
-      cur = nxt;
-      k = kn;
-    }
+    load_v(kn, nb, vr);
+    nb = nb2;
   }
 
 #pragma unroll

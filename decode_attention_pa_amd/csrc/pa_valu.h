@@ -51,7 +51,8 @@ __global__ __launch_bounds__(256) void part_valu(PartArgs a) {
   __shared__ float mmax_s[RMAX];
   __shared__ int tlo_s[RMAX], thi_s[RMAX];
 
-  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const PartItem it = part_item(a);
+  const int j = it.j, h = it.h, b = it.b;
   const int tid = threadIdx.x;
   const int L = a.seq_lens[b];
   const int q = a.query_lens[b];
