@@ -10,7 +10,7 @@ fails, an exception says so.
               scale, window, num_kv_heads, block_size, max_seq_len=...)
 
 Layouts (see include/pa_decode.h): q/out [T, H_q, D]; k_cache
-[num_blocks, H_kv, block_size, D]; v_cache [num_blocks, H_kv, D, block_size];
+[num_blocks, H_kv, block_size, D]; v_cache [num_blocks, H_kv, block_size/8, D, 8];
 block_tables int32 [B, max_blocks_per_seq]; seq_lens, query_lens int32 [B].
 """
 
@@ -192,8 +192,9 @@ def _validate(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, num_
     nb = k_cache.shape[0]
     if tuple(k_cache.shape) != (nb, num_kv_heads, block_size, D):
         raise PaError(ERR_INVALID_ARG, f"k_cache must be [num_blocks, {num_kv_heads}, {block_size}, {D}]")
-    if tuple(v_cache.shape) != (nb, num_kv_heads, D, block_size):
-        raise PaError(ERR_INVALID_ARG, f"v_cache must be [num_blocks, {num_kv_heads}, {D}, {block_size}]")
+    if block_size % 8 or tuple(v_cache.shape) != (nb, num_kv_heads, block_size // 8, D, 8):
+        raise PaError(ERR_INVALID_ARG, f"v_cache must be [num_blocks, {num_kv_heads}, "
+                                       f"{block_size // 8}, {D}, 8]")
     B = block_tables.shape[0]
     if block_tables.dim() != 2 or seq_lens.shape != (B,) or query_lens.shape != (B,):
         raise PaError(ERR_INVALID_ARG, "block_tables [B, M], seq_lens [B], query_lens [B]")

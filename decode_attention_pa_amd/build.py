@@ -30,6 +30,9 @@ def command(out: str = LIB, extra=()) -> list[str]:
         hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
         # packed fp32 VALU ops stay off: plain fp32 code only
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # matrix-core accumulators in VGPRs: the online-softmax rescale and the
+        # final normalisation then run on them in place, without AGPR copies
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         "-Wall", "-Wno-unused-function",
         "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
         *extra, *SOURCES, "-o", out,

@@ -86,7 +86,7 @@ struct PartArgs {
   void* out;                   // [T, H_q, D] (one-shot sequences)
   const void* q;               // [T, H_q, D]
   const void* k_cache;         // [num_blocks, H_kv, bs, D]
-  const void* v_cache;         // [num_blocks, H_kv, D, bs]
+  const void* v_cache;         // [num_blocks, H_kv, bs/8, D, 8]
   const int32_t* block_tables; // [B, max_blocks_per_seq]
   const int32_t* seq_lens;     // [B]
   const int32_t* query_lens;   // [B]

@@ -15,8 +15,9 @@
 //         alpha, exp-sum.  A row with nothing visible so far keeps max = -inf
 //         and never evaluates (-inf) - (-inf).
 //   PV    O^T[d, n] += sum_pos V^T[d, pos] * P^T[pos, n] — A = V^T columns
-//         straight from HBM (the V cache keeps positions contiguous per
-//         dim, so 8 positions are one 16-byte load), B = P rounded to bf16.
+//         straight from HBM (the V cache stores 8-slot groups as [D][8]
+//         tiles, so 8 positions of one dim are one 16-byte load and a lane
+//         group's 16 dims are 256 contiguous bytes), B = P rounded to bf16.
 //
 // The two QK tiles map MFMA row 4*lg + j of tile t to chunk position
 // 8*lg + 4*t + j, so after QK each lane group lg owns the 8 consecutive
@@ -35,19 +36,17 @@ namespace pa {
 
 __device__ inline bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
-// 16-byte load of streamed KV data (read once per call).
-__device__ inline u32x4 ld_stream(const uint16_t* p) {
-#ifdef PA_NT_LOADS
-  return __builtin_nontemporal_load((const u32x4*)p);
-#else
-  return *(const u32x4*)p;
-#endif
-}
+// 16-byte load of KV data.
+__device__ inline u32x4 ld_stream(const uint16_t* p) { return *(const u32x4*)p; }
 
 // Physical blocks touched by one chunk: the chunk's in-partition positions
 // [lo, hi] span at most two blocks (block_size >= 16 >= chunk / 2).  The ids
 // are wave-uniform, so they come through the scalar cache (their own wait
 // counter: no false dependence on the vector loads in flight).
+// A row's reference max is raised only when a chunk beats it by more than
+// this (log2 units): weights are then at most 2^8 before normalisation.
+constexpr float kRescaleLog2 = 8.f;
+
 struct ChunkBlocks {
   int first_idx;  // logical block index of the first in-partition position
   int first;      // its physical block
@@ -96,6 +95,10 @@ __global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
       const int g = n - i * G;
       tlo[rt] = max(ps, first_visible(L, q, i, a.window));
       thi[rt] = min(pe - 1, L - q + i);
+      if (thi[rt] < tlo[rt]) {  // row sees nothing in this partition
+        tlo[rt] = 0x7fffffff;
+        thi[rt] = -1;
+      }
       const uint16_t* qp =
           (const uint16_t*)a.q + ((size_t)(qoff + i) * a.num_q_heads + (size_t)h * G + g) * D;
 #pragma unroll
@@ -141,10 +144,12 @@ __global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
     if (p8 + 8 <= ps || p8 >= pe) p8 = max(cs, ps) & ~7;  // wholly outside: any valid group, zeroed later
     else p8 = max(p8, ps & ~7);
     const int blk = (p8 >> log2_bs) == cb.first_idx ? cb.first : cb.second;
-    const uint16_t* vp = vc + (size_t)blk * blk_stride + head_off + (p8 & bs_mask) +
-                         ((size_t)ln << log2_bs);
+    // 8-slot group (p8 & bs_mask) / 8 of the block is a [D][8] tile: the 16
+    // lanes of a lane group read 16 consecutive dims = 256 contiguous bytes
+    const uint16_t* vp = vc + (size_t)blk * blk_stride + head_off +
+                         (size_t)((p8 & bs_mask) >> 3) * (D * 8) + ln * 8;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) vr[dt] = ld_stream(vp + ((size_t)(16 * dt) << log2_bs));
+    for (int dt = 0; dt < DT; ++dt) vr[dt] = ld_stream(vp + 16 * 8 * dt);
   };
 
   f32x4 o[NRT][DT];
@@ -177,7 +182,6 @@ __global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
     const int cs = cb0 + k * kChunk;
     const int p8 = cs + 8 * lg;
     bf16x8 pb[NRT];
-    float alpha[NRT];
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
       f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
@@ -186,21 +190,35 @@ __global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
         sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[0][s]), qf[rt][s], sa, 0, 0, 0);
         sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[1][s]), qf[rt][s], sb, 0, 0, 0);
       }
+      // visible iff tlo <= t <= thi, as one unsigned comparison (rows that
+      // see nothing have tlo = 2^31 - 1, thi = -1: no t >= 0 passes)
+      const uint32_t span = (uint32_t)(thi[rt] - tlo[rt]);
       float x[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int t0 = p8 + e, t1 = p8 + 4 + e;
-        x[e] = (t0 >= tlo[rt] && t0 <= thi[rt]) ? sa[e] * scale_log2 : -INFINITY;
-        x[4 + e] = (t1 >= tlo[rt] && t1 <= thi[rt]) ? sb[e] * scale_log2 : -INFINITY;
+        x[e] = (uint32_t)(p8 + e - tlo[rt]) <= span ? sa[e] * scale_log2 : -INFINITY;
+        x[4 + e] = (uint32_t)(p8 + 4 + e - tlo[rt]) <= span ? sb[e] * scale_log2 : -INFINITY;
       }
       float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                        fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrun[rt], mx);
-      const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-      alpha[rt] = __builtin_amdgcn_exp2f(mrun[rt] - mref);
-      mrun[rt] = mnew;
+      // Lazy rescaling: the reference max of a row moves only when the chunk
+      // max exceeds it by more than kRescaleLog2 (or it is still -inf), so
+      // weights stay <= 2^kRescaleLog2 and the accumulators are rescaled on
+      // few chunks instead of every chunk.  Any reference gives the exact
+      // final result: (m, l, o) stay consistent with one another.
+      const bool grow = mx > mrun[rt] + kRescaleLog2;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        // alpha is exactly 1 for rows that keep their reference (never
+        // (-inf) - (-inf)), and 0 for a row leaving -inf
+        const float alpha = grow ? __builtin_amdgcn_exp2f(mrun[rt] - mx) : 1.f;
+        lrun[rt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[rt][dt] *= alpha;
+        mrun[rt] = grow ? mx : mrun[rt];
+      }
+      const float mref = (mrun[rt] == -INFINITY) ? 0.f : mrun[rt];
       float psum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -208,7 +226,7 @@ __global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
         pb[rt][e] = pe16;
         psum += (float)pe16;  // normalise by the weights PV actually applies
       }
-      lrun[rt] = lrun[rt] * alpha[rt] + psum;
+      lrun[rt] += psum;
     }
     load_k(kn, nb, kr);
     const ChunkBlocks nb2 = blocks_of(min(k + 2 * NW, nck - 1));
@@ -216,25 +234,29 @@ __global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
     // loads to arrive, and waiting for them earlier would serialise the
     // next chunk's K requests behind them.
     __builtin_amdgcn_sched_barrier(0);
-    // Zero V entries of positions outside [ps, pe) (only edge chunks have
-    // any) so that a zero weight never meets a stale, possibly NaN, value.
-    u32x4 keep;
+    if (cs < ps || cs + kChunk > pe) {
+      // Edge chunk: zero V entries of positions outside [ps, pe) so that a
+      // zero weight never meets a stale, possibly NaN, value.
+      u32x4 keep;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int t0 = p8 + 2 * w;
-      const uint32_t lo16 = (t0 >= ps && t0 < pe) ? 0x0000ffffu : 0u;
-      const uint32_t hi16 = (t0 + 1 >= ps && t0 + 1 < pe) ? 0xffff0000u : 0u;
-      keep[w] = lo16 | hi16;
+      for (int w = 0; w < 4; ++w) {
+        const int t0 = p8 + 2 * w;
+        const uint32_t lo16 = (t0 >= ps && t0 < pe) ? 0x0000ffffu : 0u;
+        const uint32_t hi16 = (t0 + 1 >= ps && t0 + 1 < pe) ? 0xffff0000u : 0u;
+        keep[w] = lo16 | hi16;
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) vr[dt] &= keep;
     }
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        o[rt][dt] *= alpha[rt];
-        o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vr[dt] & keep), pb[rt],
-                                                            o[rt][dt], 0, 0, 0);
-      }
+      for (int dt = 0; dt < DT; ++dt)
+        o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vr[dt]), pb[rt], o[rt][dt], 0, 0, 0);
     }
+    // Request the next V columns only after PV has read these registers
+    // (no second register copy of the chunk).
+    __builtin_amdgcn_sched_barrier(0);
     load_v(kn, nb, vr);
     nb = nb2;
   }

@@ -5,7 +5,8 @@
 // context partition of one (sequence, KV head); its G*q_b <= 64 packed rows
 // (row n = i*G + g) share every K/V chunk, which is staged through LDS:
 //
-//   stage   K chunk [32][D] and V chunk [D][32] in fp32, positions outside
+//   stage   K chunk [32][D] and V chunk [D][32] in fp32 (V read from its
+//           8-slot [D][8] tiles), positions outside
 //           the partition stored as zeros (never read from HBM)
 //   scores  one thread per (row, position): D-term dot product, masked by
 //           select to -inf outside the row's visible interval
@@ -119,8 +120,9 @@ __global__ __launch_bounds__(256) void part_valu(PartArgs a) {
       const int pos = cs + r;
       const bool ok = pos >= ps && pos < pe;
       const T* vp = nullptr;
-      if (ok) vp = vc + (size_t)phys_block(table, pos, log2_bs) * blk_stride + head_off + (pos & bs_mask);
-      for (int d = vd; d < D; d += 8) v_s[d][r] = ok ? load_elem<T>(vp + ((size_t)d << log2_bs)) : 0.f;
+      if (ok) vp = vc + (size_t)phys_block(table, pos, log2_bs) * blk_stride + head_off +
+                   (size_t)((pos & bs_mask) >> 3) * (D * 8) + (pos & 7);
+      for (int d = vd; d < D; d += 8) v_s[d][r] = ok ? load_elem<T>(vp + d * 8) : 0.f;
     }
     __syncthreads();
     for (int e = tid; e < rows_b * kChunk; e += NT) {

@@ -29,7 +29,10 @@
  *   q, out        [T, H_q, D], T = sum_b q_b; sequence b owns rows
  *                 qoff_b .. qoff_b + q_b - 1, qoff_b = q_0 + ... + q_{b-1}
  *   k_cache       [num_blocks, H_kv, block_size, D]    (one row per position)
- *   v_cache       [num_blocks, H_kv, D, block_size]    (one column per position)
+ *   v_cache       [num_blocks, H_kv, block_size/8, D, 8]: slots grouped by 8;
+ *                 slot s of a block lives at [s/8][d][s%8] (a [D, 8] tile per
+ *                 group: 16 contiguous bytes hold one dim of 8 consecutive
+ *                 positions)
  *   block_tables  int32 [B, max_blocks_per_seq]; position t of sequence b
  *                 lives in physical block block_tables[b][t / block_size] at
  *                 slot t % block_size

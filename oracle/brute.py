@@ -24,6 +24,7 @@ def brute_decode(q, k_cache, v_cache, block_tables, seq_lens, query_lens,
     H_q = len(q[0]) if len(q) else 0
     D = len(q[0][0]) if len(q) else 0
     group = H_q // num_kv_heads
+    vg = len(v_cache[0][0][0][0]) if len(v_cache) else 1   # V slot-group size
     sigma = float(_to_f32(scale))
     out = []
     row = 0
@@ -54,7 +55,7 @@ def brute_decode(q, k_cache, v_cache, block_tables, seq_lens, query_lens,
                 tot = math.fsum(wts)
                 vec = []
                 for d in range(D):
-                    acc = math.fsum(w * float(v_cache[phys][kvh][d][off])
+                    acc = math.fsum(w * float(v_cache[phys][kvh][off // vg][d][off % vg])
                                     for w, (phys, off) in zip(wts, where))
                     vec.append(acc / tot)
                 out_row.append(vec)

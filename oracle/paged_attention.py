@@ -8,7 +8,9 @@ dtype; they are widened to float64 exactly), in the layouts the library uses:
                                       qoff_b .. qoff_b + query_lens[b] - 1,
                                       qoff_b = query_lens[0] + ... + query_lens[b-1]
     k_cache      [num_blocks, H_kv, block_size, D]   (row per position)
-    v_cache      [num_blocks, H_kv, D, block_size]   (column per position)
+    v_cache      [num_blocks, H_kv, block_size/g, D, g]   (positions grouped by
+                 g: for each group of g consecutive slots, a [D, g] tile; the
+                 library uses g = 8, tests with blocks smaller than 8 use g = bs)
     block_tables [B, max_blocks_per_seq] int
     seq_lens     [B] int   context length, the query tokens included
     query_lens   [B] int   trailing query tokens of each context
@@ -75,11 +77,13 @@ def gather_keys(k_cache, table_row, positions, h, block_size):
 
 
 def gather_values(v_cache, table_row, positions, h, block_size):
-    """V rows of positions t: v_cache[table[t // bs], h, :, t % bs] -> [n, D]."""
+    """V rows of positions t: with slot s = t % bs and group size g,
+    v_cache[table[t // bs], h, s // g, :, s % g] -> [n, D]."""
+    g = v_cache.shape[-1]
     blocks = table_row[positions // block_size]
     offs = positions % block_size
-    slabs = v_cache[blocks, h]                       # [n, D, bs]
-    return slabs[np.arange(len(positions)), :, offs].astype(np.float64)
+    slabs = v_cache[blocks, h]                       # [n, bs/g, D, g]
+    return slabs[np.arange(len(positions)), offs // g, :, offs % g].astype(np.float64)
 
 
 def decode(q, k_cache, v_cache, block_tables, seq_lens, query_lens,

@@ -1,0 +1,192 @@
+"""GPU invariants that hold bit for bit, independent of tolerances.
+
+* window 1: each query token returns its own value vector exactly;
+* constant V returns the constant exactly;
+* spike probe: a key aligned with one query row and a logit gap of ~400
+  makes every other weight underflow to exactly 0, so the output equals that
+  position's value vector iff the position is visible, and is bit-identical
+  to the spike-free run iff it is not - checked at window edges, MTP
+  neighbours, block and chunk edges, across forced partition sizes;
+* NaN poison in every block no row can see (including blocks before the
+  window) leaves the output bit-identical;
+* a different physical placement of the same logical blocks, and a second
+  run, give bit-identical outputs;
+* query heads of one group with identical query vectors give identical
+  outputs; one partition versus many agree to bf16 resolution at the scale
+  of each output row (2^-6 of the row's largest magnitude).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_pa_amd as pa
+import workloads
+from oracle import paged_attention as ref
+from tests._gpu_util import BF16_TOL, compare, oracle_out, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+PATHS = [pa.PATH_MFMA, pa.PATH_VALU]
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+
+
+def mtp_workload(**over):
+    kw = dict(name="inv", dtype="bf16", batch=2, num_q_heads=4, num_kv_heads=2, head_dim=128,
+              block_size=16, query_len=3, seq_lens=(150, 77), max_seq_len=150,
+              max_blocks_per_seq=11, pool=0, seed=77, scale=1.0 / np.sqrt(128.0), windows=(0,))
+    kw.update(over)
+    return workloads.custom(**kw)
+
+
+def v_at(case, blk, h, slot):
+    return case.v_cache[blk, h, slot // 8, :, slot % 8]
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_window_one_returns_own_value(path):
+    w = mtp_workload()
+    c = workloads.make_case(w, device="cuda", window=1)
+    for P in (0, 32, 64):
+        out = run_gpu(c, path=path, part_size=P)
+        row = 0
+        for b, (L, q) in enumerate(zip(c.seq_lens_host, c.query_lens_host)):
+            for i in range(q):
+                p = L - q + i
+                blk = c.used_blocks[b][p // w.block_size]
+                for hq in range(w.num_q_heads):
+                    h = hq // (w.num_q_heads // w.num_kv_heads)
+                    assert torch.equal(out[row, hq], v_at(c, blk, h, p % w.block_size)), (path, P, b, i, hq)
+                row += 1
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_constant_values_return_constant(path):
+    w = mtp_workload()
+    for win in (0, 5, 40):
+        c = workloads.make_case(w, device="cuda", window=win)
+        c.v_cache.fill_(-0.3125)
+        for P in (0, 32, 96):
+            out = run_gpu(c, path=path, part_size=P)
+            assert torch.all(out == -0.3125), (path, win, P)
+
+
+def _spike_positions(L, q, i, window, bs):
+    p = L - q + i
+    lo = 0 if window == 0 else max(0, p + 1 - window)
+    cand = {p, p - 1, lo, lo - 1, lo + 1, p + 1, p + 2, 0,
+            (p // bs) * bs, (p // bs) * bs - 1, (p // 32) * 32, (p // 32) * 32 - 1,
+            (lo // bs) * bs, (lo // 32) * 32 + 31}
+    return sorted(t for t in cand if 0 <= t < L)
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("window", [0, 5, 40])
+def test_spike_probe_visibility(path, window):
+    w = mtp_workload(num_q_heads=2, num_kv_heads=2)   # G = 1: one query row per key head
+    base = workloads.make_case(w, device="cuda", window=window, poison=False)
+    bs = w.block_size
+    for P in (0, 32, 64):
+        clean = run_gpu(base, path=path, part_size=P).clone()
+        row0 = 0
+        for b, (L, q) in enumerate(zip(base.seq_lens_host, base.query_lens_host)):
+            for i in range(q):
+                row = row0 + i
+                lo_i, p_i = ref.visible_range(L, q, i, window)
+                for t in _spike_positions(L, q, i, window, bs):
+                    c = workloads.make_case(w, device="cuda", window=window, poison=False)
+                    blk = c.used_blocks[b][t // bs]
+                    h = 0
+                    qv = c.q[row, h].float()
+                    alpha = 400.0 / (w.scale * float(qv.dot(qv)))
+                    c.k_cache[blk, h, t % bs, :] = (alpha * qv).to(torch.bfloat16)
+                    out = run_gpu(c, path=path, part_size=P)
+                    if lo_i <= t <= p_i:
+                        expect = v_at(c, blk, h, t % bs)
+                        assert torch.equal(out[row, h], expect), (path, window, P, b, i, t)
+                    else:
+                        assert torch.equal(out[row, h], clean[row, h]), (path, window, P, b, i, t)
+            row0 += q
+    say(f"[spike] path={path} window={window}: all probes bit-exact")
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_nan_poison_of_invisible_blocks(path):
+    for win in (0, 5, 40):
+        w = mtp_workload(seq_lens=(150, 77, 33), batch=3, query_len=2)
+        c = workloads.make_case(w, device="cuda", window=win, poison=True)
+        for P in (0, 32):
+            clean = run_gpu(c, path=path, part_size=P).clone()
+            sp = ref.spans(c.tables_host.numpy(), c.seq_lens_host, c.query_lens_host, win,
+                           w.block_size)
+            visible = set(int(x) for s in sp for x in s["blocks"] if x >= 0)
+            dead = [x for x in range(c.num_blocks) if x not in visible]
+            ids = torch.tensor(dead, dtype=torch.long, device="cuda")
+            c.k_cache.index_fill_(0, ids, float("nan"))
+            c.v_cache.index_fill_(0, ids, float("nan"))
+            out = run_gpu(c, path=path, part_size=P)
+            assert torch.equal(out, clean), (path, win, P)
+            c = workloads.make_case(w, device="cuda", window=win, poison=True)
+
+
+def test_block_placement_and_rerun_are_bit_identical():
+    w = workloads.WORKLOADS["gqa_bf16"]
+    c = workloads.make_case(w, device="cuda")
+    a = run_gpu(c).clone()
+    b = run_gpu(c)
+    assert torch.equal(a, b)
+    # move every used block to a new physical slot (reverse order)
+    perm = torch.arange(c.num_blocks - 1, -1, -1, device="cuda")
+    k2 = torch.empty_like(c.k_cache)
+    v2 = torch.empty_like(c.v_cache)
+    k2[perm] = c.k_cache
+    v2[perm] = c.v_cache
+    c.k_cache, c.v_cache = k2, v2
+    c.block_tables = perm.to(torch.int32)[c.block_tables.long()]
+    assert torch.equal(run_gpu(c), a)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_identical_queries_in_a_group_agree(path):
+    w = mtp_workload(num_q_heads=8, num_kv_heads=2)
+    c = workloads.make_case(w, device="cuda", window=40)
+    G = 4
+    for g in range(1, G):
+        c.q[:, g::G] = c.q[:, 0::G]
+    out = run_gpu(c, path=path, part_size=32)
+    for g in range(1, G):
+        assert torch.equal(out[:, g::G], out[:, 0::G])
+
+
+@pytest.mark.parametrize("name,window", [("gqa_bf16", 0), ("long_splitk_bf16", 0),
+                                         ("large_block_mtp_bf16", 4096)])
+def test_one_partition_equals_many(name, window):
+    w = workloads.WORKLOADS[name]
+    c = workloads.make_case(w, device="cuda", window=window)
+    many = run_gpu(c).float()
+    one = run_gpu(c, part_size=((w.max_seq_len + 31) // 32 + 1) * 32).float()
+    # Both are the same function; they differ only in summation order and in
+    # which reference max the bf16 weights were rounded against, so the gap
+    # is bounded by bf16 resolution at the scale of each output row.
+    row_scale = torch.maximum(one.abs(), many.abs()).amax(dim=-1, keepdim=True)
+    gap = (one - many).abs()
+    worst = float((gap / row_scale.clamp_min(1e-30)).max())
+    say(f"[split] {name}: max gap {float(gap.max()):.3e}, max gap / row scale {worst:.3e}")
+    assert worst <= 2.0 ** -6, name
+
+
+@pytest.mark.parametrize("name,window", [("gqa_bf16", 0), ("long_splitk_bf16", 0)])
+def test_peaked_logits(name, window):
+    """Q scaled by 3 (logits ~ N(0, 9)): outputs of order 0.3-1, so the
+    tolerance bites harder than at N(0, 1)."""
+    w = workloads.WORKLOADS[name]
+    c = workloads.make_case(w, device="cuda", window=window, q_gain=3.0)
+    out = run_gpu(c)
+    seqs = list(range(min(w.batch, 8)))
+    exp, rows = oracle_out(c, seqs)
+    compare(out, exp, rows, BF16_TOL, f"{name} peaked")

@@ -95,7 +95,9 @@ def _sdpa_reference(a):
         t = np.arange(L)
         blk = a["block_tables"][b][t // bs]
         K = a["k_cache"][blk, :, t % bs, :]                    # [L, Hkv, D]
-        V = np.stack([a["v_cache"][blk[j], :, :, t[j] % bs] for j in range(L)])  # [L, Hkv, D]
+        g = a["v_cache"].shape[-1]
+        V = np.stack([a["v_cache"][blk[j], :, (t[j] % bs) // g, :, (t[j] % bs) % g]
+                      for j in range(L)])                      # [L, Hkv, D]
         Q = a["q"][qoff:qoff + ql]                             # [ql, Hq, D]
         i = np.arange(ql)[:, None]
         p = L - ql + i
@@ -146,9 +148,9 @@ def test_golden_visible_sets_through_outputs():
         nb = -(-L // bs)
         D = L
         k = np.ones((nb, 1, bs, D))
-        v = np.zeros((nb, 1, D, bs))
+        v = np.zeros((nb, 1, 1, D, bs))            # one slot group per block
         for t in range(L):
-            v[t // bs, 0, t, t % bs] = 1.0
+            v[t // bs, 0, 0, t, t % bs] = 1.0
         a = dict(q=np.ones((ql, 1, D)), k_cache=k, v_cache=v,
                  block_tables=np.arange(nb)[None, :], seq_lens=np.array([L]),
                  query_lens=np.array([ql]), scale=1.0, window=win, num_kv_heads=1, block_size=bs)
@@ -165,10 +167,10 @@ def _one_seq(q, K, V, window=0, scale=1.0, bs=2, ql=1):
     nb = -(-L // bs)
     perm = np.random.default_rng(7).permutation(nb + 3)
     k = np.full((nb + 3, 1, bs, D), np.nan)
-    v = np.full((nb + 3, 1, D, bs), np.nan)
+    v = np.full((nb + 3, 1, 1, D, bs), np.nan)     # one slot group per block
     for t in range(L):
         k[perm[t // bs], 0, t % bs, :] = K[t]
-        v[perm[t // bs], 0, :, t % bs] = V[t]
+        v[perm[t // bs], 0, 0, :, t % bs] = V[t]
     return dict(q=np.asarray(q, float).reshape(ql, 1, D), k_cache=k, v_cache=v,
                 block_tables=perm[None, :nb], seq_lens=np.array([L]), query_lens=np.array([ql]),
                 scale=scale, window=window, num_kv_heads=1, block_size=bs)
@@ -246,7 +248,9 @@ def test_window_one_returns_own_value():
             p = L - ql + i
             blk = a["block_tables"][b][p // w.block_size]
             for hq in range(w.num_q_heads):
-                np.testing.assert_array_equal(out[row, hq], a["v_cache"][blk, hq // G, :, p % w.block_size])
+                g = a["v_cache"].shape[-1]
+                s = p % w.block_size
+                np.testing.assert_array_equal(out[row, hq], a["v_cache"][blk, hq // G, s // g, :, s % g])
             row += 1
 
 

@@ -7,7 +7,8 @@ can consume what it produces without sharing code.
 Layouts (the library's contract):
     q, out        [T, H_q, D], T = sum(query_lens), packed in sequence order
     k_cache       [num_blocks, H_kv, block_size, D]
-    v_cache       [num_blocks, H_kv, D, block_size]
+    v_cache       [num_blocks, H_kv, block_size/8, D, 8]  (8-slot groups, each a
+                  [D, 8] tile; blocks smaller than 8 use one group of bs)
     block_tables  int32 [B, max_blocks_per_seq]
     seq_lens      int32 [B]  (context length, query tokens included)
     query_lens    int32 [B]
@@ -189,7 +190,8 @@ def make_case(w: Workload | str, device="cpu", window: int | None = None,
     if q_gain != 1.0:
         q.copy_((q.float() * q_gain).to(dt))
     k = torch.empty((pool, w.num_kv_heads, bs, w.head_dim), dtype=dt, device=dev)
-    v = torch.empty((pool, w.num_kv_heads, w.head_dim, bs), dtype=dt, device=dev)
+    g = min(8, bs)
+    v = torch.empty((pool, w.num_kv_heads, bs // g, w.head_dim, g), dtype=dt, device=dev)
     _fill_normal(k, vg)
     _fill_normal(v, vg)
     if poison:
@@ -202,7 +204,8 @@ def make_case(w: Workload | str, device="cpu", window: int | None = None,
             if tail and used[b]:
                 last = used[b][-1]
                 k[last, :, tail:, :] = float("nan")
-                v[last, :, :, tail:] = float("nan")
+                slots = torch.arange(tail, bs, device=dev)
+                v[last, :, slots // g, :, slots % g] = float("nan")
     return Case(
         w=w, window=int(window), q=q, k_cache=k, v_cache=v,
         block_tables=tables.to(dev), seq_lens=torch.tensor(lens, dtype=torch.int32, device=dev),
