@@ -76,6 +76,50 @@ def load_traffic(workload: str, window: int):
     return rec.get("bytes_per_launch")
 
 
+def _counter_rows(path):
+    import csv
+    for root, _, files in os.walk(path):
+        for f in files:
+            if f.endswith("counter_collection.csv"):
+                yield from csv.DictReader(open(os.path.join(root, f)))
+
+
+def ingest_counters(workload: str, window: int, fetch_dir: str, write_dir: str,
+                    command: str) -> dict:
+    """Turns two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per
+    dispatch) of ``bench.py --copy-calibration`` into HBM bytes per launch of
+    the partition kernel.  Each counter is scaled by what it reads for the
+    plain 1 GiB device copy in the same run (known: 1 GiB read, 1 GiB
+    written).  Writes the record into profiles/traffic.json."""
+    gib_kib = float(1 << 20)
+    rec = {"workload": workload, "window": window, "kernel_hash": kernel_source_hash(),
+           "command": command}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        copy, part = [], []
+        for r in _counter_rows(d):
+            if r["Counter_Name"] != name:
+                continue
+            v = float(r["Counter_Value"])
+            if "copyBuffer" in r["Kernel_Name"] and v > gib_kib / 8:
+                copy.append(v)
+            elif "part_mfma" in r["Kernel_Name"] or "part_valu" in r["Kernel_Name"]:
+                part.append(v)
+        if not copy or not part:
+            raise SystemExit(f"{name}: no calibration copy or partition kernel in {d}")
+        calib = sum(copy) / len(copy)
+        scale = gib_kib / calib
+        per = sum(part[1:]) / max(len(part) - 1, 1) if len(part) > 1 else part[0]  # first is cold
+        rec[name] = {"copy_kib": round(calib, 2), "scale": round(scale, 5),
+                     "partition_kib_raw": round(per, 2),
+                     "partition_bytes": int(per * scale * 1024), "dispatches": len(part)}
+    rec["bytes_per_launch"] = rec["FETCH_SIZE"]["partition_bytes"] + rec["WRITE_SIZE"]["partition_bytes"]
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    allrec = json.load(open(path)) if os.path.exists(path) else {}
+    allrec[f"{workload}:w{window}"] = rec
+    json.dump(allrec, open(path, "w"), indent=1, sort_keys=True)
+    return rec
+
+
 def cpu_baseline(case, out_gpu, budget_s: float, per_call_bytes: int) -> dict:
     """The float64 oracle, as it stands, on a bounded sample of the workload's
     sequences (host cores of this machine), scaled to µs per full call by
@@ -133,7 +177,16 @@ def main(argv=None):
                          "the value is then the mean per-call event time")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain 1 GiB device copies (counter calibration)")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="(no GPU) record rocprofv3 FETCH_SIZE/WRITE_SIZE runs of this "
+                         "workload into profiles/traffic.json and exit")
+    ap.add_argument("--ingest-command", default="", help="command line that produced them")
     a = ap.parse_args(argv)
+    if a.ingest_counters:
+        w = a.workload
+        win = a.window if a.window is not None else __import__("workloads").WORKLOADS[w].windows[0]
+        print(json.dumps(ingest_counters(w, win, *a.ingest_counters, a.ingest_command)))
+        return 0
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); this library has no "
               "multi-GPU path.", file=sys.stderr)

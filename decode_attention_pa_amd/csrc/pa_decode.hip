@@ -295,12 +295,15 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
     r.rows = p.rows;
     r.num_parts = p.num_parts;
     r.part_size = p.part_size;
-    const bool narrow = p.num_parts <= pa::kNarrowMaxParts;
-    const dim3 rgrid = narrow ? dim3(hkv, d->batch)
-                              : dim3(p.rows * (d->head_dim / pa::kReduceSlice), hkv, d->batch);
-#define PA_REDUCE(T, D)                                                                      \
-  if (narrow) hipLaunchKernelGGL((pa::lse_reduce_narrow<T, D>), rgrid, dim3(256), 0, s, r); \
-  else hipLaunchKernelGGL((pa::lse_reduce_wide<T, D>), rgrid, dim3(256), 0, s, r);
+    const int gp = pa::reduce_group_lanes(p.num_parts);
+    const int units = p.rows * (d->head_dim / 4);
+    const dim3 rgrid((units + 256 / gp - 1) / (256 / gp), hkv, d->batch);
+#define PA_REDUCE(T, D)                                                                     \
+  switch (gp) {                                                                            \
+    case 1: hipLaunchKernelGGL((pa::lse_reduce<T, D, 1>), rgrid, dim3(256), 0, s, r); break; \
+    case 16: hipLaunchKernelGGL((pa::lse_reduce<T, D, 16>), rgrid, dim3(256), 0, s, r); break; \
+    default: hipLaunchKernelGGL((pa::lse_reduce<T, D, 256>), rgrid, dim3(256), 0, s, r); break; \
+  }
     if (d->dtype == PA_F32) {
       if (d->head_dim == 64) { PA_REDUCE(float, 64) } else { PA_REDUCE(float, 128) }
     } else {

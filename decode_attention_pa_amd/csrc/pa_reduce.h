@@ -17,144 +17,125 @@
 
 namespace pa {
 
-// Two launch shapes, chosen on the host from the partition count NP:
-//
-//  * narrow (NP <= kNarrowMaxParts): one 256-thread workgroup per (sequence,
-//    KV head); wave w merges rows w, w+4, ...; each lane owns D/64 dims and
-//    requests all of its partitions' slices at once.  Few workgroups, one
-//    round trip per row.
-//  * wide: one workgroup per (32-dim slice, packed row, KV head, sequence);
-//    32 partition groups x 8 lanes x float4, several loads in flight per
-//    lane, partition groups summed in a fixed order afterwards.  Many lanes
-//    per row when a row has hundreds of partitions.
-constexpr int kNarrowMaxParts = 32;
-constexpr int kReduceSlice = 32;   // dims per wide workgroup
-constexpr int kReduceGroups = 32;  // partition groups per wide workgroup
+// One thread group per output unit = (packed row n, 4 consecutive dims) of
+// one (sequence, KV head); the GP threads of a group split the partitions
+// (GP = 1, 16 or 256, chosen on the host from NP) and combine their partial
+// sums by a fixed butterfly / tree, so results are deterministic.  Each
+// thread requests all of its partitions' float4 slices before using them.
+// Grid: x = unit blocks of 256/GP units, y = KV head, z = sequence.
+template <int GP>
+struct GroupReduce {
+  // max and sum over the GP threads of a group (all lanes of the group are
+  // active together: they share one output row)
+  __device__ static float max(float x, float* lds) {
+    if constexpr (GP == 1) return x;
+    if constexpr (GP <= 64) {
+#pragma unroll
+      for (int off = GP / 2; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+      return x;
+    } else {
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+      const int wave = threadIdx.x >> 6;
+      __syncthreads();
+      if ((threadIdx.x & 63) == 0) lds[wave] = x;
+      __syncthreads();
+      return fmaxf(fmaxf(lds[0], lds[1]), fmaxf(lds[2], lds[3]));
+    }
+  }
+  __device__ static float sum(float x, float* lds) {
+    if constexpr (GP == 1) return x;
+    if constexpr (GP <= 64) {
+#pragma unroll
+      for (int off = GP / 2; off > 0; off >>= 1) x += __shfl_xor(x, off);
+      return x;
+    } else {
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+      const int wave = threadIdx.x >> 6;
+      __syncthreads();
+      if ((threadIdx.x & 63) == 0) lds[wave] = x;
+      __syncthreads();
+      return ((lds[0] + lds[1]) + lds[2]) + lds[3];
+    }
+  }
+};
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void lse_reduce_narrow(ReduceArgs a) {
-  constexpr int DPL = D / 64;  // dims per lane
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+template <typename T, int D, int GP>
+__global__ __launch_bounds__(256) void lse_reduce(ReduceArgs a) {
+  constexpr int UPW = 256 / GP;  // units per workgroup
+  constexpr int D4 = D / 4;
+  constexpr int U = 4;           // partitions in flight per thread per step
+  __shared__ float lds[4];
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
   const int L = a.seq_lens[b];
   const int q = a.query_lens[b];
   const int G = a.group;
   const SeqView sv = seq_view(L, q, a.window, a.part_size);
   const int np = min(sv.nparts, a.num_parts);
   if (np <= 1) return;  // the partition kernel wrote these rows directly
-  const int qoff = wave_row_offset(a.query_lens, b);
+  const int qoff = wave_row_offset(a.query_lens, b);  // all lanes still active
+  const int unit = blockIdx.x * UPW + tid / GP;
+  const int gp = tid % GP;
+  const int n = unit / D4, d4 = unit % D4;
+  if (n >= G * q) return;  // whole groups (and, for GP = 256, whole blocks) leave together
   const size_t base = ((size_t)b * a.num_kv_heads + h) * a.num_parts;
-  for (int n = wave; n < G * q; n += 4) {
-    float mj[kNarrowMaxParts], lj[kNarrowMaxParts];
-    float o[kNarrowMaxParts][DPL];
-#pragma unroll
-    for (int jj = 0; jj < kNarrowMaxParts; ++jj) {
-      mj[jj] = -INFINITY;
-      lj[jj] = 0.f;
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) o[jj][e] = 0.f;
-      if (jj < np) {
-        const size_t w = (base + jj) * a.rows + n;
-        mj[jj] = a.ws_m[w];
-        lj[jj] = a.ws_l[w];
-        const float* op = a.ws_o + w * D + lane * DPL;
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) o[jj][e] = op[e];
-      }
-    }
-    float M = -INFINITY;
-#pragma unroll
-    for (int jj = 0; jj < kNarrowMaxParts; ++jj) M = fmaxf(M, mj[jj]);
-    const float mref = (M == -INFINITY) ? 0.f : M;
-    float acc[DPL], den = 0.f;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
-#pragma unroll
-    for (int jj = 0; jj < kNarrowMaxParts; ++jj) {
-      const float f = (mj[jj] == -INFINITY) ? 0.f : exp2f(mj[jj] - mref) * lj[jj];
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[e] += f * o[jj][e];
-      den += f;
-    }
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    const int i = n / G, g = n - i * G;
-    T* op = (T*)a.out + ((size_t)(qoff + i) * a.num_q_heads + (size_t)h * G + g) * D + lane * DPL;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) store_elem<T>(op + e, acc[e] * inv);
-  }
-}
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void lse_reduce_wide(ReduceArgs a) {
-  constexpr int NS = D / kReduceSlice;
-  const int slice = blockIdx.x % NS;
-  const int n = blockIdx.x / NS;
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int L = a.seq_lens[b];
-  const int q = a.query_lens[b];
-  const int G = a.group;
-  if (n >= G * q) return;
-  const SeqView sv = seq_view(L, q, a.window, a.part_size);
-  const int np = min(sv.nparts, a.num_parts);
-  if (np <= 1) return;  // the partition kernel wrote this row directly
-
-  __shared__ float red[4];
-  __shared__ f32x4 sacc[kReduceGroups][8];
-  __shared__ float sden[kReduceGroups];
-  const size_t base = ((size_t)b * a.num_kv_heads + h) * a.num_parts;
-  float M = -INFINITY;
-  for (int jj = tid; jj < np; jj += 256) M = fmaxf(M, a.ws_m[(base + jj) * a.rows + n]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  if (lane == 0) red[wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float mref = (M == -INFINITY) ? 0.f : M;
-
-  const int grp = tid >> 3;        // partition group
-  const int d4 = (tid & 7) * 4;    // dims d4 .. d4+3 of the slice
+  // One pass: each thread keeps a running reference max mt over its own
+  // partitions (rescaling its sums when it grows), then the group agrees on
+  // M = max mt and every thread rescales by 2^(mt - M) before the sums.
+  float mt = -INFINITY;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  constexpr int U = 4;
-  for (int j0 = grp; j0 < np; j0 += kReduceGroups * U) {
-    float f[U];
+  for (int j0 = gp; j0 < np; j0 += GP * U) {
+    float mj[U], lj[U];
     f32x4 o[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int jj = j0 + u * kReduceGroups;
-      f[u] = 0.f;
+      const int jj = j0 + u * GP;
+      mj[u] = -INFINITY;
+      lj[u] = 0.f;
       o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (jj < np) {
         const size_t w = (base + jj) * a.rows + n;
-        const float mj = a.ws_m[w];
-        f[u] = (mj == -INFINITY) ? 0.f : exp2f(mj - mref) * a.ws_l[w];
-        o[u] = *(const f32x4*)(a.ws_o + w * D + slice * kReduceSlice + d4);
+        mj[u] = a.ws_m[w];
+        lj[u] = a.ws_l[w];
+        o[u] = *(const f32x4*)(a.ws_o + w * D + d4 * 4);
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      acc += f[u] * o[u];
-      den += f[u];
+      if (mj[u] == -INFINITY) continue;  // partition where this row sees nothing
+      if (mj[u] > mt) {
+        const float r = exp2f(mt - mj[u]);  // 0 while mt = -inf
+        acc *= r;
+        den *= r;
+        mt = mj[u];
+      }
+      const float f = exp2f(mj[u] - mt) * lj[u];
+      acc += f * o[u];
+      den += f;
     }
   }
-  sacc[grp][tid & 7] = acc;
-  if ((tid & 7) == 0) sden[grp] = den;
-  // every lane of the wave takes part in the prefix sum's shuffles
-  const int qoff = wave_row_offset(a.query_lens, b);
-  __syncthreads();
-  if (tid >= kReduceSlice) return;
-  // thread tid finalises dim tid of the slice
-  float s = 0.f, tot = 0.f;
-#pragma unroll 8
-  for (int g = 0; g < kReduceGroups; ++g) {
-    s += sacc[g][tid >> 2][tid & 3];
-    tot += sden[g];
-  }
-  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  const float M = GroupReduce<GP>::max(mt, lds);
+  const float r = (mt == -INFINITY) ? 0.f : exp2f(mt - M);
+  acc *= r;
+  den *= r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc[e] = GroupReduce<GP>::sum(acc[e], lds);
+  den = GroupReduce<GP>::sum(den, lds);
+  if (gp != 0) return;
+  const float inv = den > 0.f ? 1.f / den : 0.f;
   const int i = n / G, g = n - i * G;
-  T* op = (T*)a.out + ((size_t)(qoff + i) * a.num_q_heads + (size_t)h * G + g) * D;
-  store_elem<T>(op + slice * kReduceSlice + tid, s * inv);
+  T* op = (T*)a.out + ((size_t)(qoff + i) * a.num_q_heads + (size_t)h * G + g) * D + d4 * 4;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) store_elem<T>(op + e, acc[e] * inv);
+}
+
+// Partition lanes per output unit for a given partition count.
+inline int reduce_group_lanes(int num_parts) {
+  return num_parts <= 32 ? 1 : (num_parts <= 256 ? 16 : 256);
 }
 
 struct SpanArgs {

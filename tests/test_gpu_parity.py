@@ -208,3 +208,18 @@ def test_full_workload(name, window, nsample):
     compare(out, exp, rows, BF16_TOL, f"{name} w={window} seqs={len(seqs)}")
     # rows not compared must still be finite and written
     assert torch.isfinite(out.float()).all()
+
+
+@pytest.mark.parametrize("P", [32, 64, 256, 4096])
+def test_reduce_lane_modes(P):
+    """Partition counts in every regime of the merge kernel (1, 16 or 256
+    lanes per output unit): 3 sequences of up to 20000 positions."""
+    w = small(11, head_dim=128, num_q_heads=16, num_kv_heads=2, query_len=2, batch=3,
+              seq_lens=(20000, 4000, 129), block_size=32, max_seq_len=20000,
+              max_blocks_per_seq=626)
+    for win in (0, 3000):
+        c = workloads.make_case(w, device="cuda", window=win)
+        np_ = -(-(20000 + 31) // P) if win == 0 else -(-(win + 1 + 31) // P)
+        say(f"[case] reduce modes P={P} window={win} partitions={np_}")
+        exp, rows = oracle_out(c)
+        compare(run_gpu(c, part_size=P), exp, rows, BF16_TOL, f"reduce P={P} w={win}")
