@@ -34,12 +34,15 @@ DEFAULT_WORKLOAD = "gqa_bf16"
 
 
 def kernel_source_hash() -> str:
+    """Fingerprint of the partition kernels' sources and compile flags (the
+    kernel the roofline and traffic figures describe)."""
+    from decode_attention_pa_amd import build as b
     d = os.path.join(ROOT, "decode_attention_pa_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".h", ".hip")):
-            h.update(f.encode())
-            h.update(open(os.path.join(d, f), "rb").read())
+    for f in ("pa_common.h", "pa_mfma.h", "pa_valu.h"):
+        h.update(f.encode())
+        h.update(open(os.path.join(d, f), "rb").read())
+    h.update(" ".join(a for a in b.command("x") if a.startswith("-")).encode())
     return h.hexdigest()[:16]
 
 
