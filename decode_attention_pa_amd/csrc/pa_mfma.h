@@ -47,31 +47,34 @@ __device__ inline u32x4 ld_stream(const uint16_t* p) { return *(const u32x4*)p; 
 // this (log2 units): weights are then at most 2^8 before normalisation.
 constexpr float kRescaleLog2 = 8.f;
 
+// Largest batch the persistent schedule handles (its per-sequence prefix sums
+// live in shared memory); larger batches use the grid schedule.
+constexpr int kPsMaxBatch = 1024;
+
 struct ChunkBlocks {
   int first_idx;  // logical block index of the first in-partition position
   int first;      // its physical block
   int second;     // physical block of the last in-partition position
 };
 
+// One run: partitions j_first .. j_last of unit (sequence b, KV head h),
+// processed as one stretch of positions by the NW waves of the workgroup.
+// A sequence with a single partition writes `out`; otherwise the run's state
+// goes to workspace slot j_first and slots j_first+1 .. j_last are marked
+// empty (max = -inf), so the merge sees one state per run.  All waves of the
+// workgroup call this with the same arguments.
 template <int D, int NRT, int NW>
-__global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
+__device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L, int q, int qoff,
+                                         const SeqView& sv, int j_first, int j_last) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
-  const PartItem it = part_item(a);
-  const int j = it.j, h = it.h, b = it.b;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ln = lane & 15, lg = lane >> 4;
-
-  const int L = a.seq_lens[b];
-  const int q = a.query_lens[b];
-  const SeqView sv = seq_view(L, q, a.window, a.part_size);
-  if (j >= sv.nparts) return;  // empty partition: contributes nothing
-  int ps, pe;
-  partition_range(sv, j, a.part_size, &ps, &pe);
-  const int cb0 = sv.base + j * a.part_size;  // chunk-aligned partition start
+  const int ps = max(sv.lo, sv.base + j_first * a.part_size);
+  const int pe = min(sv.hi, sv.base + (j_last + 1) * a.part_size);
+  const int cb0 = sv.base + j_first * a.part_size;  // chunk-aligned run start
   const int nck = (pe - cb0 + kChunk - 1) / kChunk;
-  const int qoff = wave_row_offset(a.query_lens, b);
   const int G = a.group;
   const int rows_b = G * q;
   const int log2_bs = a.log2_bs;
@@ -286,57 +289,162 @@ __global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
         for (int dt = 0; dt < DT; ++dt) sm_o[wave - 1][rt][dt][lane] = o[rt][dt];
     }
     __syncthreads();
-    if (wave != 0) return;
+    if (wave == 0) {
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      const int n = rt * 16 + ln;
-      float M = -INFINITY;
+      for (int rt = 0; rt < NRT; ++rt) {
+        const int n = rt * 16 + ln;
+        float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][n]);
-      const float mref = (M == -INFINITY) ? 0.f : M;
-      const float f0 = __builtin_amdgcn_exp2f(mrun[rt] - mref);
-      float l = lrun[rt] * f0;
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][n]);
+        const float mref = (M == -INFINITY) ? 0.f : M;
+        const float f0 = __builtin_amdgcn_exp2f(mrun[rt] - mref);
+        float l = lrun[rt] * f0;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[rt][dt] *= f0;
+        for (int dt = 0; dt < DT; ++dt) o[rt][dt] *= f0;
 #pragma unroll
-      for (int w = 1; w < NW; ++w) {
-        const float fw = __builtin_amdgcn_exp2f(sm_m[w][n] - mref);
-        l += sm_l[w][n] * fw;
+        for (int w = 1; w < NW; ++w) {
+          const float fw = __builtin_amdgcn_exp2f(sm_m[w][n] - mref);
+          l += sm_l[w][n] * fw;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[rt][dt] += fw * sm_o[w - 1][rt][dt][lane];
+          for (int dt = 0; dt < DT; ++dt) o[rt][dt] += fw * sm_o[w - 1][rt][dt][lane];
+        }
+        mrun[rt] = M;
+        lrun[rt] = l;
       }
-      mrun[rt] = M;
-      lrun[rt] = l;
     }
   }
 
-  const bool one_shot = (sv.nparts == 1);
+  if (wave == 0) {
+    const bool one_shot = (sv.nparts == 1);
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    const int n = rt * 16 + ln;
-    if (n >= rows_b) continue;
-    const float inv = lrun[rt] > 0.f ? 1.f / lrun[rt] : 0.f;
-    if (one_shot) {
-      const int i = n / G;
-      const int g = n - i * G;
-      uint16_t* op = (uint16_t*)a.out + ((size_t)(qoff + i) * a.num_q_heads + (size_t)h * G + g) * D;
+    for (int rt = 0; rt < NRT; ++rt) {
+      const int n = rt * 16 + ln;
+      if (n >= rows_b) continue;
+      const float inv = lrun[rt] > 0.f ? 1.f / lrun[rt] : 0.f;
+      if (one_shot) {
+        const int i = n / G;
+        const int g = n - i * G;
+        uint16_t* op =
+            (uint16_t*)a.out + ((size_t)(qoff + i) * a.num_q_heads + (size_t)h * G + g) * D;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        bf16x4 v;
+        for (int dt = 0; dt < DT; ++dt) {
+          bf16x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[rt][dt][e] * inv);
-        *(bf16x4*)(op + 16 * dt + 4 * lg) = v;
+          for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[rt][dt][e] * inv);
+          *(bf16x4*)(op + 16 * dt + 4 * lg) = v;
+        }
+      } else {
+        const size_t slot0 = ((size_t)b * a.num_kv_heads + h) * a.num_parts;
+        const size_t w = (slot0 + j_first) * a.rows + n;
+        if (lg == 0) {
+          a.ws_m[w] = mrun[rt];
+          a.ws_l[w] = lrun[rt];
+          for (int jj = j_first + 1; jj <= j_last; ++jj) {  // merged into this run
+            a.ws_m[(slot0 + jj) * a.rows + n] = -INFINITY;
+            a.ws_l[(slot0 + jj) * a.rows + n] = 0.f;
+          }
+        }
+        float* op = a.ws_o + w * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) *(f32x4*)(op + 16 * dt + 4 * lg) = o[rt][dt] * inv;
       }
-    } else {
-      const size_t w = (((size_t)b * a.num_kv_heads + h) * a.num_parts + j) * a.rows + n;
-      if (lg == 0) {
-        a.ws_m[w] = mrun[rt];
-        a.ws_l[w] = lrun[rt];
-      }
-      float* op = a.ws_o + w * D;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) *(f32x4*)(op + 16 * dt + 4 * lg) = o[rt][dt] * inv;
     }
+  }
+}
+
+// Grid schedule: one workgroup per (partition, sequence, KV head).
+template <int D, int NRT, int NW>
+__global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
+  const PartItem it = part_item(a);
+  const int L = a.seq_lens[it.b];
+  const int q = a.query_lens[it.b];
+  const SeqView sv = seq_view(L, q, a.window, a.part_size);
+  if (it.j >= sv.nparts) return;  // empty partition: contributes nothing
+  const int qoff = wave_row_offset(a.query_lens, it.b);
+  mfma_run<D, NRT, NW>(a, it.b, it.h, L, q, qoff, sv, it.j, it.j);
+}
+
+// Persistent schedule (aiter PR #2914: "PS" decode): a grid of about one
+// resident set of workgroups.  The partitions of all units form one list,
+// unit-major ((sequence, KV head), then partition); workgroup w takes the
+// contiguous share [w*I/W, (w+1)*I/W) of the I partitions and runs each
+// unit's stretch of it as one run.  Shares differ by at most one partition,
+// so there is no tail of late workgroups, and a workgroup's set-up is paid
+// once per unit it touches rather than once per partition.
+template <int D, int NRT, int NW>
+__global__ __launch_bounds__(64 * NW) void part_mfma_ps(PartArgs a) {
+  constexpr int NT = 64 * NW;
+  __shared__ int s_np[kPsMaxBatch + 1];  // exclusive prefix of partitions per sequence
+  __shared__ int s_q[kPsMaxBatch + 1];   // exclusive prefix of query tokens (q/out row)
+  __shared__ int s_wave[2][NW];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int B = a.batch;
+  // Block-wide exclusive scan of (partitions, query tokens) over sequences.
+  const int per = (B + NT - 1) / NT;
+  const int k0 = min(B, tid * per), k1 = min(B, k0 + per);
+  int cnt_np = 0, cnt_q = 0;
+  for (int k = k0; k < k1; ++k) {
+    const int q = a.query_lens[k];
+    cnt_np += seq_view(a.seq_lens[k], q, a.window, a.part_size).nparts;
+    cnt_q += q;
+  }
+  int inc_np = cnt_np, inc_q = cnt_q;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t_np = __shfl_up(inc_np, off), t_q = __shfl_up(inc_q, off);
+    if (lane >= off) {
+      inc_np += t_np;
+      inc_q += t_q;
+    }
+  }
+  if (lane == 63) {
+    s_wave[0][wave] = inc_np;
+    s_wave[1][wave] = inc_q;
+  }
+  __syncthreads();
+  int run_np = inc_np - cnt_np, run_q = inc_q - cnt_q;
+  for (int w = 0; w < wave; ++w) {
+    run_np += s_wave[0][w];
+    run_q += s_wave[1][w];
+  }
+  for (int k = k0; k < k1; ++k) {
+    s_np[k] = run_np;
+    s_q[k] = run_q;
+    const int q = a.query_lens[k];
+    run_np += seq_view(a.seq_lens[k], q, a.window, a.part_size).nparts;
+    run_q += q;
+  }
+  if (tid == NT - 1) {
+    s_np[B] = run_np;
+    s_q[B] = run_q;
+  }
+  __syncthreads();
+
+  const int H = a.num_kv_heads;
+  const long total = (long)H * s_np[B];
+  const long W = gridDim.x;
+  long i0 = (long)blockIdx.x * total / W;
+  const long i1 = ((long)blockIdx.x + 1) * total / W;
+  while (i0 < i1) {
+    // sequence of partition i0: the last b with H * s_np[b] <= i0
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((long)H * s_np[mid] <= i0) lo = mid;
+      else hi = mid - 1;
+    }
+    const int b = __builtin_amdgcn_readfirstlane(lo);
+    const int np_b = s_np[b + 1] - s_np[b];
+    const long rel = i0 - (long)H * s_np[b];
+    const int h = __builtin_amdgcn_readfirstlane((int)(rel / np_b));
+    const int j1 = __builtin_amdgcn_readfirstlane((int)(rel - (long)h * np_b));
+    const int j2 = (int)min((long)np_b - 1, (long)j1 + (i1 - i0) - 1);
+    const int L = a.seq_lens[b];
+    const int q = a.query_lens[b];
+    const SeqView sv = seq_view(L, q, a.window, a.part_size);
+    mfma_run<D, NRT, NW>(a, b, h, L, q, s_q[b], sv, j1, j2);
+    __syncthreads();  // the next run reuses the merge's shared memory
+    i0 += j2 - j1 + 1;
   }
 }
 

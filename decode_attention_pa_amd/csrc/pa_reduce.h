@@ -122,9 +122,31 @@ __global__ __launch_bounds__(256) void lse_reduce(ReduceArgs a) {
   const float r = (mt == -INFINITY) ? 0.f : exp2f(mt - M);
   acc *= r;
   den *= r;
+  if constexpr (GP == 256) {
+    // the whole workgroup is one group: reduce the five sums per wave, then
+    // once through shared memory
+    __shared__ float part[4][5];
+    float v[5] = {acc[0], acc[1], acc[2], acc[3], den};
 #pragma unroll
-  for (int e = 0; e < 4; ++e) acc[e] = GroupReduce<GP>::sum(acc[e], lds);
-  den = GroupReduce<GP>::sum(den, lds);
+    for (int e = 0; e < 5; ++e) {
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) v[e] += __shfl_xor(v[e], off);
+    }
+    const int wave = tid >> 6;
+    if ((tid & 63) == 0) {
+#pragma unroll
+      for (int e = 0; e < 5; ++e) part[wave][e] = v[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 5; ++e) v[e] = ((part[0][e] + part[1][e]) + part[2][e]) + part[3][e];
+    acc = f32x4{v[0], v[1], v[2], v[3]};
+    den = v[4];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = GroupReduce<GP>::sum(acc[e], lds);
+    den = GroupReduce<GP>::sum(den, lds);
+  }
   if (gp != 0) return;
   const float inv = den > 0.f ? 1.f / den : 0.f;
   const int i = n / G, g = n - i * G;

@@ -107,7 +107,8 @@ typedef struct pa_plan {
   int32_t num_parts;          /* partition-grid extent per (sequence, KV head) */
   int32_t waves;              /* 64-lane waves per partition workgroup */
   int32_t one_shot;           /* 1: a single partition writes out directly */
-  int32_t reserved;
+  int32_t persistent;         /* 1: persistent schedule (resident grid, balanced partition
+                                 shares); 0: one workgroup per partition */
   uint64_t workspace_bytes;   /* bytes pa_decode needs in `workspace` (0 if one_shot) */
 } pa_plan;
 
@@ -116,7 +117,8 @@ typedef struct pa_options {
   int32_t path;               /* pa_path; AUTO picks by dtype and R */
   int32_t part_size;          /* force the partition size (multiple of 32), 0 = auto */
   int32_t waves;              /* force waves per workgroup (1, 2 or 4), 0 = auto */
-  int32_t reserved;
+  int32_t schedule;           /* 0 = auto, 1 = one workgroup per partition, 2 = persistent
+                                 (matrix-core path, batch <= 1024) */
   void* event_begin;          /* hipEvent_t recorded on the stream just before the
                                  partition kernel, or NULL */
   void* event_end;            /* hipEvent_t recorded just after it, or NULL */

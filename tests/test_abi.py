@@ -139,10 +139,27 @@ def test_plan_rejects_block_sizes(lib, bs, code):
 def test_plan_rejects_negative_window_and_bad_options(lib):
     w = workloads.WORKLOADS["gqa_bf16"]
     for kw, win in [({}, -1), (dict(part_size=48), 0), (dict(part_size=-32), 0),
-                    (dict(waves=3), 0), (dict(path=9), 0)]:
+                    (dict(waves=3), 0), (dict(path=9), 0), (dict(schedule=3), 0)]:
         with pytest.raises(pa.PaError) as e:
             pa.plan(dims_of(w), win, 8, 16, **kw)
         assert e.value.status == pa.ERR_INVALID_ARG
+
+
+def test_persistent_schedule_choice(lib):
+    gqa = workloads.WORKLOADS["gqa_bf16"]
+    assert pa.plan(dims_of(gqa), 0, 8, 16)["persistent"] == 1          # 256 units, split
+    assert pa.plan(dims_of(gqa), 0, 8, 16, schedule=pa.SCHED_GRID)["persistent"] == 0
+    long = workloads.WORKLOADS["long_splitk_bf16"]
+    assert pa.plan(dims_of(long), 0, 1, 16)["persistent"] == 0         # one unit
+    assert pa.plan(dims_of(long), 0, 1, 16, schedule=pa.SCHED_PERSISTENT)["persistent"] == 1
+    tiny = workloads.WORKLOADS["tiny_f32"]
+    with pytest.raises(pa.PaError) as e:                              # vector path: grid only
+        pa.plan(dims_of(tiny), 0, 1, 16, schedule=pa.SCHED_PERSISTENT)
+    assert e.value.status == pa.ERR_UNSUPPORTED
+    with pytest.raises(pa.PaError) as e:
+        pa.plan(dims_of(gqa, batch=1025, max_blocks_per_seq=512), 0, 8, 16,
+                schedule=pa.SCHED_PERSISTENT)
+    assert e.value.status == pa.ERR_UNSUPPORTED
 
 
 def test_plan_rejects_mfma_for_fp32(lib):

@@ -28,6 +28,8 @@ from tests._gpu_util import BF16_TOL, compare, oracle_out, run_gpu, say
 pytestmark = pytest.mark.gpu
 
 PATHS = [pa.PATH_MFMA, pa.PATH_VALU]
+KERNELS = [(pa.PATH_MFMA, pa.SCHED_GRID), (pa.PATH_MFMA, pa.SCHED_PERSISTENT),
+           (pa.PATH_VALU, pa.SCHED_GRID)]
 
 
 @pytest.fixture(autouse=True)
@@ -85,14 +87,14 @@ def _spike_positions(L, q, i, window, bs):
     return sorted(t for t in cand if 0 <= t < L)
 
 
-@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("path,sched", KERNELS)
 @pytest.mark.parametrize("window", [0, 5, 40])
-def test_spike_probe_visibility(path, window):
+def test_spike_probe_visibility(path, sched, window):
     w = mtp_workload(num_q_heads=2, num_kv_heads=2)   # G = 1: one query row per key head
     base = workloads.make_case(w, device="cuda", window=window, poison=False)
     bs = w.block_size
     for P in (0, 32, 64):
-        clean = run_gpu(base, path=path, part_size=P).clone()
+        clean = run_gpu(base, path=path, part_size=P, schedule=sched).clone()
         row0 = 0
         for b, (L, q) in enumerate(zip(base.seq_lens_host, base.query_lens_host)):
             for i in range(q):
@@ -105,7 +107,7 @@ def test_spike_probe_visibility(path, window):
                     qv = c.q[row, h].float()
                     alpha = 400.0 / (w.scale * float(qv.dot(qv)))
                     c.k_cache[blk, h, t % bs, :] = (alpha * qv).to(torch.bfloat16)
-                    out = run_gpu(c, path=path, part_size=P)
+                    out = run_gpu(c, path=path, part_size=P, schedule=sched)
                     if lo_i <= t <= p_i:
                         expect = v_at(c, blk, h, t % bs)
                         assert torch.equal(out[row, h], expect), (path, window, P, b, i, t)
@@ -115,13 +117,13 @@ def test_spike_probe_visibility(path, window):
     say(f"[spike] path={path} window={window}: all probes bit-exact")
 
 
-@pytest.mark.parametrize("path", PATHS)
-def test_nan_poison_of_invisible_blocks(path):
+@pytest.mark.parametrize("path,sched", KERNELS)
+def test_nan_poison_of_invisible_blocks(path, sched):
     for win in (0, 5, 40):
         w = mtp_workload(seq_lens=(150, 77, 33), batch=3, query_len=2)
         c = workloads.make_case(w, device="cuda", window=win, poison=True)
         for P in (0, 32):
-            clean = run_gpu(c, path=path, part_size=P).clone()
+            clean = run_gpu(c, path=path, part_size=P, schedule=sched).clone()
             sp = ref.spans(c.tables_host.numpy(), c.seq_lens_host, c.query_lens_host, win,
                            w.block_size)
             visible = set(int(x) for s in sp for x in s["blocks"] if x >= 0)
@@ -129,8 +131,8 @@ def test_nan_poison_of_invisible_blocks(path):
             ids = torch.tensor(dead, dtype=torch.long, device="cuda")
             c.k_cache.index_fill_(0, ids, float("nan"))
             c.v_cache.index_fill_(0, ids, float("nan"))
-            out = run_gpu(c, path=path, part_size=P)
-            assert torch.equal(out, clean), (path, win, P)
+            out = run_gpu(c, path=path, part_size=P, schedule=sched)
+            assert torch.equal(out, clean), (path, sched, win, P)
             c = workloads.make_case(w, device="cuda", window=win, poison=True)
 
 
@@ -169,7 +171,7 @@ def test_one_partition_equals_many(name, window):
     w = workloads.WORKLOADS[name]
     c = workloads.make_case(w, device="cuda", window=window)
     many = run_gpu(c).float()
-    one = run_gpu(c, part_size=((w.max_seq_len + 31) // 32 + 1) * 32).float()
+    one = run_gpu(c, part_size=((w.max_seq_len + 31) // 32 + 1) * 32, schedule=pa.SCHED_GRID).float()
     # Both are the same function; they differ only in summation order and in
     # which reference max the bf16 weights were rounded against, so the gap
     # is bounded by bf16 resolution at the scale of each output row.

@@ -55,17 +55,21 @@ def test_tiny_f32(window):
         compare(run_gpu(c, part_size=P), exp, rows, F32_TOL, f"tiny_f32 w={window} P={P}")
 
 
-@pytest.mark.parametrize("path", [pa.PATH_MFMA, pa.PATH_VALU])
+KERNELS = [(pa.PATH_MFMA, pa.SCHED_GRID), (pa.PATH_MFMA, pa.SCHED_PERSISTENT),
+           (pa.PATH_VALU, pa.SCHED_GRID)]
+
+
+@pytest.mark.parametrize("path,sched", KERNELS)
 @pytest.mark.parametrize("seed", range(10))
-def test_small_bf16(seed, path):
+def test_small_bf16(seed, path, sched):
     w = small(seed)
     for win in (0, 1, 5, 37, 100000):
         c = workloads.make_case(w, device="cuda", window=win)
-        say(f"[case] small seed={seed} path={path} window={win} {w}")
+        say(f"[case] small seed={seed} path={path} schedule={sched} window={win} {w}")
         exp, rows = oracle_out(c)
         for P in (0, 32, 64):
-            compare(run_gpu(c, path=path, part_size=P), exp, rows, BF16_TOL,
-                    f"small{seed} path={path} w={win} P={P}")
+            compare(run_gpu(c, path=path, part_size=P, schedule=sched), exp, rows, BF16_TOL,
+                    f"small{seed} path={path} sched={sched} w={win} P={P}")
 
 
 @pytest.mark.parametrize("seed", range(4))
@@ -101,10 +105,10 @@ def test_max_rows_and_edge_lengths():
         for win in (0, 2, 40):
             c = workloads.make_case(w, device="cuda", window=win)
             exp, rows = oracle_out(c)
-            for path in (pa.PATH_MFMA, pa.PATH_VALU):
+            for path, sched in KERNELS:
                 for P in (0, 32):
-                    compare(run_gpu(c, path=path, part_size=P), exp, rows, BF16_TOL,
-                            f"edges D={D} w={win} path={path} P={P}")
+                    compare(run_gpu(c, path=path, part_size=P, schedule=sched), exp, rows,
+                            BF16_TOL, f"edges D={D} w={win} path={path} sched={sched} P={P}")
 
 
 def test_debug_spans_bit_exact():
@@ -189,12 +193,13 @@ FULL = [("gqa_bf16", 0, None), ("swa_mtp_bf16", 128, None), ("long_splitk_bf16",
         ("large_block_mtp_bf16", 4096, 24), ("large_block_mtp_bf16", 0, 2)]
 
 
+@pytest.mark.parametrize("sched", [pa.SCHED_AUTO, pa.SCHED_GRID])
 @pytest.mark.parametrize("name,window,nsample", FULL)
-def test_full_workload(name, window, nsample):
+def test_full_workload(name, window, nsample, sched):
     w = workloads.WORKLOADS[name]
-    say(f"[case] full {name} window={window}")
+    say(f"[case] full {name} window={window} schedule={sched}")
     c = workloads.make_case(w, device="cuda", window=window)
-    out = run_gpu(c)
+    out = run_gpu(c, schedule=sched)
     B = w.batch
     if nsample is None:
         seqs = list(range(B))
@@ -210,8 +215,9 @@ def test_full_workload(name, window, nsample):
     assert torch.isfinite(out.float()).all()
 
 
+@pytest.mark.parametrize("sched", [pa.SCHED_GRID, pa.SCHED_PERSISTENT])
 @pytest.mark.parametrize("P", [32, 64, 256, 4096])
-def test_reduce_lane_modes(P):
+def test_reduce_lane_modes(P, sched):
     """Partition counts in every regime of the merge kernel (1, 16 or 256
     lanes per output unit): 3 sequences of up to 20000 positions."""
     w = small(11, head_dim=128, num_q_heads=16, num_kv_heads=2, query_len=2, batch=3,
@@ -222,4 +228,5 @@ def test_reduce_lane_modes(P):
         np_ = -(-(20000 + 31) // P) if win == 0 else -(-(win + 1 + 31) // P)
         say(f"[case] reduce modes P={P} window={win} partitions={np_}")
         exp, rows = oracle_out(c)
-        compare(run_gpu(c, part_size=P), exp, rows, BF16_TOL, f"reduce P={P} w={win}")
+        compare(run_gpu(c, part_size=P, schedule=sched), exp, rows, BF16_TOL,
+                f"reduce P={P} sched={sched} w={win}")
