@@ -93,6 +93,7 @@ struct PartArgs {
   float* ws_m;                 // [B, H_kv, NP, R] running max, log2 domain
   float* ws_l;                 // [B, H_kv, NP, R] exp-sum
   float* ws_o;                 // [B, H_kv, NP, R, D] normalised partial output
+  int* ws_runs;                // [B, H_kv] states per unit (persistent schedule only)
   float scale_log2;            // scale * log2(e)
   int window;
   int num_q_heads;
@@ -133,6 +134,7 @@ struct ReduceArgs {
   const float* ws_m;
   const float* ws_l;
   const float* ws_o;
+  const int* ws_runs;   // states per unit, or null: every partition holds one
   int window;
   int num_q_heads;
   int num_kv_heads;

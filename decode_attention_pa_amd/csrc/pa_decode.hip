@@ -174,7 +174,8 @@ pa_status make_plan(const pa_dims* d, int32_t window, int32_t hkv, int32_t bs, i
     r.workspace_bytes = 0;
   } else {
     const uint64_t states = (uint64_t)d->batch * hkv * r.num_parts * r.rows;
-    r.workspace_bytes = 2 * align256(states * 4) + align256(states * d->head_dim * 4);
+    r.workspace_bytes = 2 * align256(states * 4) + align256(states * d->head_dim * 4) +
+                        (r.persistent ? align256((uint64_t)d->batch * hkv * 4) : 0);
   }
   *p = r;
   return PA_OK;
@@ -290,6 +291,9 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
   a.ws_m = p.one_shot ? nullptr : (float*)ws;
   a.ws_l = p.one_shot ? nullptr : (float*)(ws + align256(states * 4));
   a.ws_o = p.one_shot ? nullptr : (float*)(ws + 2 * align256(states * 4));
+  a.ws_runs = (p.one_shot || !p.persistent)
+                  ? nullptr
+                  : (int*)(ws + 2 * align256(states * 4) + align256(states * d->head_dim * 4));
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.window = window;
   a.num_q_heads = d->num_q_heads;
@@ -338,6 +342,7 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
     r.ws_m = a.ws_m;
     r.ws_l = a.ws_l;
     r.ws_o = a.ws_o;
+    r.ws_runs = a.ws_runs;
     r.window = window;
     r.num_q_heads = d->num_q_heads;
     r.num_kv_heads = hkv;
@@ -345,7 +350,8 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
     r.rows = p.rows;
     r.num_parts = p.num_parts;
     r.part_size = p.part_size;
-    const int gp = pa::reduce_group_lanes(p.num_parts);
+    // persistent: a unit has about one state per workgroup share it crosses
+    const int gp = pa::reduce_group_lanes(p.persistent ? std::min(p.num_parts, 32) : p.num_parts);
     const int units = p.rows * (d->head_dim / 4);
     const dim3 rgrid((units + 256 / gp - 1) / (256 / gp), hkv, d->batch);
 #define PA_REDUCE(T, D)                                                                     \

@@ -59,13 +59,13 @@ struct ChunkBlocks {
 
 // One run: partitions j_first .. j_last of unit (sequence b, KV head h),
 // processed as one stretch of positions by the NW waves of the workgroup.
-// A sequence with a single partition writes `out`; otherwise the run's state
-// goes to workspace slot j_first and slots j_first+1 .. j_last are marked
-// empty (max = -inf), so the merge sees one state per run.  All waves of the
-// workgroup call this with the same arguments.
+// With `write_out` (the run is the whole unit) it writes `out`; otherwise its
+// state (max, exp-sum, normalised output) goes to workspace slot `slot` of
+// the unit.  All waves of the workgroup call this with the same arguments.
 template <int D, int NRT, int NW>
 __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L, int q, int qoff,
-                                         const SeqView& sv, int j_first, int j_last) {
+                                         const SeqView& sv, int j_first, int j_last, int slot,
+                                         bool write_out) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   const int lane = threadIdx.x & 63;
@@ -315,7 +315,7 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
   }
 
   if (wave == 0) {
-    const bool one_shot = (sv.nparts == 1);
+    const bool one_shot = write_out;
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
       const int n = rt * 16 + ln;
@@ -334,15 +334,10 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
           *(bf16x4*)(op + 16 * dt + 4 * lg) = v;
         }
       } else {
-        const size_t slot0 = ((size_t)b * a.num_kv_heads + h) * a.num_parts;
-        const size_t w = (slot0 + j_first) * a.rows + n;
+        const size_t w = (((size_t)b * a.num_kv_heads + h) * a.num_parts + slot) * a.rows + n;
         if (lg == 0) {
           a.ws_m[w] = mrun[rt];
           a.ws_l[w] = lrun[rt];
-          for (int jj = j_first + 1; jj <= j_last; ++jj) {  // merged into this run
-            a.ws_m[(slot0 + jj) * a.rows + n] = -INFINITY;
-            a.ws_l[(slot0 + jj) * a.rows + n] = 0.f;
-          }
         }
         float* op = a.ws_o + w * D;
 #pragma unroll
@@ -361,7 +356,7 @@ __global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
   const SeqView sv = seq_view(L, q, a.window, a.part_size);
   if (it.j >= sv.nparts) return;  // empty partition: contributes nothing
   const int qoff = wave_row_offset(a.query_lens, it.b);
-  mfma_run<D, NRT, NW>(a, it.b, it.h, L, q, qoff, sv, it.j, it.j);
+  mfma_run<D, NRT, NW>(a, it.b, it.h, L, q, qoff, sv, it.j, it.j, it.j, sv.nparts == 1);
 }
 
 // Persistent schedule (aiter PR #2914: "PS" decode): a grid of about one
@@ -370,7 +365,10 @@ __global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
 // contiguous share [w*I/W, (w+1)*I/W) of the I partitions and runs each
 // unit's stretch of it as one run.  Shares differ by at most one partition,
 // so there is no tail of late workgroups, and a workgroup's set-up is paid
-// once per unit it touches rather than once per partition.
+// once per unit it touches rather than once per partition.  A run that is a
+// whole unit writes `out`; otherwise it stores its state in slot k = its
+// ordinal among the unit's runs, and the unit's last run records the number
+// of states for the merge (0 when the unit was written directly).
 template <int D, int NRT, int NW>
 __global__ __launch_bounds__(64 * NW) void part_mfma_ps(PartArgs a) {
   constexpr int NT = 64 * NW;
@@ -422,7 +420,10 @@ __global__ __launch_bounds__(64 * NW) void part_mfma_ps(PartArgs a) {
 
   const int H = a.num_kv_heads;
   const long total = (long)H * s_np[B];
-  const long W = gridDim.x;
+  // Shares over at most `total` workgroups, so that every share is non-empty
+  // and a run's ordinal within its unit stays below the unit's partition count.
+  const long W = min((long)gridDim.x, total);
+  if ((long)blockIdx.x >= W) return;
   long i0 = (long)blockIdx.x * total / W;
   const long i1 = ((long)blockIdx.x + 1) * total / W;
   while (i0 < i1) {
@@ -442,7 +443,17 @@ __global__ __launch_bounds__(64 * NW) void part_mfma_ps(PartArgs a) {
     const int L = a.seq_lens[b];
     const int q = a.query_lens[b];
     const SeqView sv = seq_view(L, q, a.window, a.part_size);
-    mfma_run<D, NRT, NW>(a, b, h, L, q, s_q[b], sv, j1, j2);
+    // ordinal of this run among the unit's runs: this workgroup minus the
+    // workgroup whose share holds the unit's first partition (item A);
+    // share w starts at floor(w*I/W), so item i lies in share ceil((i+1)W/I)-1
+    const long A = (long)H * s_np[b] + (long)h * np_b;
+    const long w_first = ((A + 1) * W + total - 1) / total - 1;
+    const int slot = (int)((long)blockIdx.x - w_first);
+    const bool whole = (j1 == 0 && j2 == np_b - 1);
+    mfma_run<D, NRT, NW>(a, b, h, L, q, s_q[b], sv, j1, j2, slot, whole);
+    // (one-shot plans have no workspace: every unit is whole and no merge runs)
+    if (j2 == np_b - 1 && tid == 0 && a.ws_runs != nullptr)
+      a.ws_runs[(size_t)b * H + h] = whole ? 0 : slot + 1;
     __syncthreads();  // the next run reuses the merge's shared memory
     i0 += j2 - j1 + 1;
   }

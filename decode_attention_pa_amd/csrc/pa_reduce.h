@@ -73,8 +73,10 @@ __global__ __launch_bounds__(256) void lse_reduce(ReduceArgs a) {
   const int q = a.query_lens[b];
   const int G = a.group;
   const SeqView sv = seq_view(L, q, a.window, a.part_size);
-  const int np = min(sv.nparts, a.num_parts);
-  if (np <= 1) return;  // the partition kernel wrote these rows directly
+  // states to merge: one per partition, or the unit's run count
+  const int np = a.ws_runs ? min(a.ws_runs[(size_t)b * a.num_kv_heads + h], a.num_parts)
+                           : (sv.nparts > 1 ? min(sv.nparts, a.num_parts) : 0);
+  if (np <= 0) return;  // the partition kernel wrote these rows directly
   const int qoff = wave_row_offset(a.query_lens, b);  // all lanes still active
   const int unit = blockIdx.x * UPW + tid / GP;
   const int gp = tid % GP;
@@ -89,17 +91,21 @@ __global__ __launch_bounds__(256) void lse_reduce(ReduceArgs a) {
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
   for (int j0 = gp; j0 < np; j0 += GP * U) {
+    // states first; partial outputs only for slots where the row saw
+    // something (max > -inf)
     float mj[U], lj[U];
     f32x4 o[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int jj = j0 + u * GP;
-      mj[u] = -INFINITY;
+      mj[u] = jj < np ? a.ws_m[(base + jj) * a.rows + n] : -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
       lj[u] = 0.f;
       o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (jj < np) {
-        const size_t w = (base + jj) * a.rows + n;
-        mj[u] = a.ws_m[w];
+      if (mj[u] != -INFINITY) {
+        const size_t w = (base + j0 + u * GP) * a.rows + n;
         lj[u] = a.ws_l[w];
         o[u] = *(const f32x4*)(a.ws_o + w * D + d4 * 4);
       }
@@ -155,9 +161,9 @@ __global__ __launch_bounds__(256) void lse_reduce(ReduceArgs a) {
   for (int e = 0; e < 4; ++e) store_elem<T>(op + e, acc[e] * inv);
 }
 
-// Partition lanes per output unit for a given partition count.
-inline int reduce_group_lanes(int num_parts) {
-  return num_parts <= 32 ? 1 : (num_parts <= 256 ? 16 : 256);
+// Partition lanes per output unit for a given number of states per unit.
+inline int reduce_group_lanes(int num_states) {
+  return num_states <= 32 ? 1 : (num_states <= 256 ? 16 : 256);
 }
 
 struct SpanArgs {

@@ -76,7 +76,8 @@ def test_plan_covers_longest_span(lib, name):
         else:
             states = w.batch * w.num_kv_heads * p["num_parts"] * p["rows"]
             al = lambda x: (x + 255) // 256 * 256
-            assert p["workspace_bytes"] == 2 * al(4 * states) + al(4 * states * w.head_dim)
+            runs = al(4 * w.batch * w.num_kv_heads) if p["persistent"] else 0
+            assert p["workspace_bytes"] == 2 * al(4 * states) + al(4 * states * w.head_dim) + runs
         expect_path = pa.PATH_VALU if w.dtype == "f32" else pa.PATH_MFMA
         assert p["path"] == expect_path
 
