@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--window W]
                     [--no-cpu-baseline] [--flush] [--path auto|mfma|valu] [--part-size P]
+                    [--schedule auto|grid|persistent] [--loads auto|cached|streaming]
 
 A step is one pa_decode call (partition kernel + LSE reduce) over the
 workload's batch, inputs resident in HBM.  Prints ONE JSON line: µs per call,
@@ -34,12 +35,13 @@ DEFAULT_WORKLOAD = "gqa_bf16"
 
 
 def kernel_source_hash() -> str:
-    """Fingerprint of the partition kernels' sources and compile flags (the
-    kernel the roofline and traffic figures describe)."""
+    """Fingerprint of the partition kernels' sources, the plan that launches
+    them and the compile flags (what the roofline and traffic figures
+    describe)."""
     from decode_attention_pa_amd import build as b
     d = os.path.join(ROOT, "decode_attention_pa_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("pa_common.h", "pa_mfma.h", "pa_valu.h"):
+    for f in ("pa_common.h", "pa_mfma.h", "pa_valu.h", "pa_decode.hip"):
         h.update(f.encode())
         h.update(open(os.path.join(d, f), "rb").read())
     h.update(" ".join(a for a in b.command("x") if a.startswith("-")).encode())
@@ -173,6 +175,8 @@ def main(argv=None):
     ap.add_argument("--path", default="auto", choices=["auto", "mfma", "valu"])
     ap.add_argument("--part-size", type=int, default=0)
     ap.add_argument("--waves", type=int, default=0)
+    ap.add_argument("--schedule", default="auto", choices=["auto", "grid", "persistent"])
+    ap.add_argument("--loads", default="auto", choices=["auto", "cached", "streaming"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--flush", action="store_true",
@@ -212,7 +216,11 @@ def main(argv=None):
     call = pa.Prepared(out, case.q, case.k_cache, case.v_cache, case.block_tables, case.seq_lens,
                        case.query_lens, case.scale, window, w.num_kv_heads, w.block_size,
                        max_seq_len=w.max_seq_len, max_query_len=w.query_len, path=path,
-                       part_size=a.part_size, waves=a.waves)
+                       part_size=a.part_size, waves=a.waves,
+                       schedule={"auto": 0, "grid": pa.SCHED_GRID,
+                                 "persistent": pa.SCHED_PERSISTENT}[a.schedule],
+                       loads={"auto": 0, "cached": pa.LOADS_CACHED,
+                              "streaming": pa.LOADS_STREAMING}[a.loads])
     # flush = reading 1 GiB evicts the workload from L2 and the 256 MB MALL
     # with clean lines (a write would leave dirty lines behind to write back)
     flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda") if a.flush else None

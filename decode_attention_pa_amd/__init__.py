@@ -56,7 +56,7 @@ class Plan(ctypes.Structure):
                 ("span_max", ctypes.c_int32), ("part_size", ctypes.c_int32),
                 ("num_parts", ctypes.c_int32), ("waves", ctypes.c_int32),
                 ("one_shot", ctypes.c_int32), ("persistent", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_uint64)]
+                ("streaming", ctypes.c_int32), ("workspace_bytes", ctypes.c_uint64)]
 
     def as_dict(self) -> dict:
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -65,6 +65,7 @@ class Plan(ctypes.Structure):
 class Options(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("part_size", ctypes.c_int32),
                 ("waves", ctypes.c_int32), ("schedule", ctypes.c_int32),
+                ("loads", ctypes.c_int32),
                 ("event_begin", ctypes.c_void_p), ("event_end", ctypes.c_void_p)]
 
 
@@ -120,11 +121,12 @@ def make_dims(batch, num_q_heads, head_dim, max_query_len, max_seq_len, max_bloc
 
 
 SCHED_AUTO, SCHED_GRID, SCHED_PERSISTENT = 0, 1, 2
+LOADS_AUTO, LOADS_CACHED, LOADS_STREAMING = 0, 1, 2
 
 
 def make_options(path=0, part_size=0, waves=0, event_begin=None, event_end=None,
-                 schedule=0) -> Options:
-    return Options(int(path), int(part_size), int(waves), int(schedule),
+                 schedule=0, loads=0) -> Options:
+    return Options(int(path), int(part_size), int(waves), int(schedule), int(loads),
                    _event_handle(event_begin), _event_handle(event_end))
 
 
@@ -207,7 +209,7 @@ def _validate(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, num_
 def decode(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, scale, window,
            num_kv_heads, block_size, max_seq_len, max_query_len=None, workspace=None,
            stream=None, path=0, part_size=0, waves=0, event_begin=None, event_end=None,
-           schedule=0):
+           schedule=0, loads=0):
     """Runs pa_decode_ex on torch tensors; returns ``out``.
 
     ``max_seq_len`` / ``max_query_len`` are host-known upper bounds of the
@@ -221,7 +223,7 @@ def decode(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, scale, 
         max_query_len = int(q.shape[0]) if block_tables.shape[0] else 1
         max_query_len = max(1, min(max_query_len, int(max_seq_len)))
     dims = dims_for(q, k_cache, block_tables, max_query_len, max_seq_len)
-    opts = make_options(path, part_size, waves, event_begin, event_end, schedule)
+    opts = make_options(path, part_size, waves, event_begin, event_end, schedule, loads)
     need = workspace_size(dims, window, num_kv_heads, block_size, path=path,
                           part_size=part_size, waves=waves, schedule=schedule)
     if workspace is None and need:
@@ -270,16 +272,17 @@ class Prepared:
     def __init__(self, out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, scale, window,
                  num_kv_heads, block_size, max_seq_len, max_query_len, workspace=None,
                  stream=None, path=0, part_size=0, waves=0, event_begin=None, event_end=None,
-                 schedule=0):
+                 schedule=0, loads=0):
         import torch
         _validate(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, num_kv_heads,
                   block_size)
         self.dims = dims_for(q, k_cache, block_tables, max_query_len, max_seq_len)
-        self.opts = make_options(path, part_size, waves, event_begin, event_end, schedule)
+        self.opts = make_options(path, part_size, waves, event_begin, event_end, schedule, loads)
         self._events = (event_begin, event_end)
         self.plan = plan(self.dims, window, num_kv_heads, block_size,
                          num_cus=torch.cuda.get_device_properties(q.device).multi_processor_count,
-                         path=path, part_size=part_size, waves=waves, schedule=schedule)
+                         path=path, part_size=part_size, waves=waves, schedule=schedule,
+                         loads=loads)
         need = workspace_size(self.dims, window, num_kv_heads, block_size, path=path,
                               part_size=part_size, waves=waves, schedule=schedule)
         if workspace is None and need:

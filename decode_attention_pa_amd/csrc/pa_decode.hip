@@ -52,6 +52,9 @@ int ilog2_exact(int x) {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
+// MI355X last-level cache (MALL, AMD Infinity Cache): 256 MB.
+constexpr int64_t kLastLevelCacheBytes = 256ll << 20;
+
 // Host-visible argument checks shared by every entry point.
 pa_status check_shape(const pa_dims* d, int32_t window, int32_t num_kv_heads, int32_t block_size) {
   if (!d) return fail(PA_ERR_INVALID_ARG, "dims is NULL");
@@ -166,6 +169,16 @@ pa_status make_plan(const pa_dims* d, int32_t window, int32_t hkv, int32_t bs, i
     pc = std::min<int64_t>(pc, 128);
     r.part_size = (int32_t)(pc * pa::kChunk);
   }
+  // KV load form.  Distinct KV bytes a call can read: every sequence's span,
+  // but no more than the whole pool.  Above the last-level cache (MI355X
+  // MALL, 256 MB) nothing is reused and non-temporal loads stream faster.
+  const int loads_req = o ? o->loads : 0;
+  if (loads_req < 0 || loads_req > 2) return fail(PA_ERR_INVALID_ARG, "loads %d unknown", loads_req);
+  const int64_t elem = d->dtype == PA_F32 ? 4 : 2;
+  const int64_t kv_positions = std::min<int64_t>((int64_t)d->batch * r.span_max,
+                                                 (int64_t)d->num_blocks * bs);
+  const bool big = kv_positions * hkv * d->head_dim * 2 * elem > kLastLevelCacheBytes;
+  r.streaming = r.path != PA_PATH_MFMA ? 0 : (loads_req == 2 ? 1 : (loads_req == 1 ? 0 : big));
   r.num_parts = (int32_t)std::max<int64_t>(1, cdiv(span_cover, r.part_size));
   if (r.num_parts == 1) r.part_size = (int32_t)(cdiv(span_cover, pa::kChunk) * pa::kChunk);
   r.one_shot = r.num_parts == 1;
@@ -219,30 +232,37 @@ int resident_wgs(const void* fn, int threads, int cus) {
   return cus;
 }
 
-template <int D, int NRT, int NW>
+template <int D, int NRT, int NW, bool STREAM>
 void launch_mfma_inst(dim3 grid, bool persistent, int cus, hipStream_t s, const pa::PartArgs& a) {
   if (persistent) {
-    const void* fn = (const void*)pa::part_mfma_ps<D, NRT, NW>;
+    const void* fn = (const void*)pa::part_mfma_ps<D, NRT, NW, STREAM>;
     const dim3 pgrid(resident_wgs(fn, 64 * NW, cus));
-    hipLaunchKernelGGL((pa::part_mfma_ps<D, NRT, NW>), pgrid, dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((pa::part_mfma_ps<D, NRT, NW, STREAM>), pgrid, dim3(64 * NW), 0, s, a);
   } else {
-    hipLaunchKernelGGL((pa::part_mfma<D, NRT, NW>), grid, dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((pa::part_mfma<D, NRT, NW, STREAM>), grid, dim3(64 * NW), 0, s, a);
+  }
+}
+
+template <int D, bool STREAM>
+bool launch_mfma_loads(int nrt, int nw, dim3 grid, bool persistent, int cus, hipStream_t s,
+                    const pa::PartArgs& a) {
+  switch (nrt * 8 + nw) {
+    case 1 * 8 + 1: launch_mfma_inst<D, 1, 1, STREAM>(grid, persistent, cus, s, a); return true;
+    case 1 * 8 + 2: launch_mfma_inst<D, 1, 2, STREAM>(grid, persistent, cus, s, a); return true;
+    case 1 * 8 + 4: launch_mfma_inst<D, 1, 4, STREAM>(grid, persistent, cus, s, a); return true;
+    case 2 * 8 + 1: launch_mfma_inst<D, 2, 1, STREAM>(grid, persistent, cus, s, a); return true;
+    case 2 * 8 + 2: launch_mfma_inst<D, 2, 2, STREAM>(grid, persistent, cus, s, a); return true;
+    case 3 * 8 + 1: launch_mfma_inst<D, 3, 1, STREAM>(grid, persistent, cus, s, a); return true;
+    case 4 * 8 + 1: launch_mfma_inst<D, 4, 1, STREAM>(grid, persistent, cus, s, a); return true;
+    default: return false;
   }
 }
 
 template <int D>
-bool launch_mfma(int nrt, int nw, dim3 grid, bool persistent, int cus, hipStream_t s,
-                 const pa::PartArgs& a) {
-  switch (nrt * 8 + nw) {
-    case 1 * 8 + 1: launch_mfma_inst<D, 1, 1>(grid, persistent, cus, s, a); return true;
-    case 1 * 8 + 2: launch_mfma_inst<D, 1, 2>(grid, persistent, cus, s, a); return true;
-    case 1 * 8 + 4: launch_mfma_inst<D, 1, 4>(grid, persistent, cus, s, a); return true;
-    case 2 * 8 + 1: launch_mfma_inst<D, 2, 1>(grid, persistent, cus, s, a); return true;
-    case 2 * 8 + 2: launch_mfma_inst<D, 2, 2>(grid, persistent, cus, s, a); return true;
-    case 3 * 8 + 1: launch_mfma_inst<D, 3, 1>(grid, persistent, cus, s, a); return true;
-    case 4 * 8 + 1: launch_mfma_inst<D, 4, 1>(grid, persistent, cus, s, a); return true;
-    default: return false;
-  }
+bool launch_mfma(int nrt, int nw, dim3 grid, bool persistent, bool streaming, int cus,
+                 hipStream_t s, const pa::PartArgs& a) {
+  return streaming ? launch_mfma_loads<D, true>(nrt, nw, grid, persistent, cus, s, a)
+                   : launch_mfma_loads<D, false>(nrt, nw, grid, persistent, cus, s, a);
 }
 
 pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -273,10 +293,10 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
   if (log_enabled())
     std::fprintf(stderr,
                  "[pa_decode] B=%d Hq=%d Hkv=%d D=%d bs=%d w=%d R=%d span_max=%d path=%s P=%d NP=%d "
-                 "waves=%d one_shot=%d persistent=%d ws=%llu cus=%d\n",
+                 "waves=%d one_shot=%d persistent=%d streaming=%d ws=%llu cus=%d\n",
                  d->batch, d->num_q_heads, hkv, d->head_dim, bs, window, p.rows, p.span_max,
                  p.path == PA_PATH_MFMA ? "mfma" : "valu", p.part_size, p.num_parts, p.waves,
-                 p.one_shot, p.persistent, (unsigned long long)p.workspace_bytes, cus);
+                 p.one_shot, p.persistent, p.streaming, (unsigned long long)p.workspace_bytes, cus);
 
   const uint64_t states = (uint64_t)d->batch * hkv * p.num_parts * p.rows;
   char* ws = (char*)workspace;
@@ -318,8 +338,9 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
   const int nrt = (p.rows + 15) / 16;
   bool ok = true;
   if (p.path == PA_PATH_MFMA) {
-    ok = d->head_dim == 64 ? launch_mfma<64>(nrt, p.waves, grid, p.persistent, cus, s, a)
-                           : launch_mfma<128>(nrt, p.waves, grid, p.persistent, cus, s, a);
+    ok = d->head_dim == 64
+             ? launch_mfma<64>(nrt, p.waves, grid, p.persistent, p.streaming, cus, s, a)
+             : launch_mfma<128>(nrt, p.waves, grid, p.persistent, p.streaming, cus, s, a);
   } else if (d->dtype == PA_F32) {
     if (d->head_dim == 64) hipLaunchKernelGGL((pa::part_valu<float, 64>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((pa::part_valu<float, 128>), grid, dim3(256), 0, s, a);

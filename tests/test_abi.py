@@ -140,7 +140,8 @@ def test_plan_rejects_block_sizes(lib, bs, code):
 def test_plan_rejects_negative_window_and_bad_options(lib):
     w = workloads.WORKLOADS["gqa_bf16"]
     for kw, win in [({}, -1), (dict(part_size=48), 0), (dict(part_size=-32), 0),
-                    (dict(waves=3), 0), (dict(path=9), 0), (dict(schedule=3), 0)]:
+                    (dict(waves=3), 0), (dict(path=9), 0), (dict(schedule=3), 0),
+                    (dict(loads=3), 0), (dict(loads=-1), 0)]:
         with pytest.raises(pa.PaError) as e:
             pa.plan(dims_of(w), win, 8, 16, **kw)
         assert e.value.status == pa.ERR_INVALID_ARG
@@ -161,6 +162,32 @@ def test_persistent_schedule_choice(lib):
         pa.plan(dims_of(gqa, batch=1025, max_blocks_per_seq=512), 0, 8, 16,
                 schedule=pa.SCHED_PERSISTENT)
     assert e.value.status == pa.ERR_UNSUPPORTED
+
+
+def test_streaming_loads_choice(lib):
+    # Non-temporal KV loads when min(B * span_max, pool positions) x H_kv x D
+    # x 2 (K and V) x 2 bytes exceeds the 256 MB last-level cache.
+    gqa = workloads.WORKLOADS["gqa_bf16"]            # pool of 10899 blocks: 681 MiB
+    assert pa.plan(dims_of(gqa, num_blocks=10899), 0, 8, 16)["streaming"] == 1
+    assert pa.plan(dims_of(gqa, num_blocks=10899), 0, 8, 16,
+                   loads=pa.LOADS_CACHED)["streaming"] == 0
+    # the same shape over a small pool: 2000 x 16 positions x 4 KiB = 125 MiB
+    assert pa.plan(dims_of(gqa, num_blocks=2000), 0, 8, 16)["streaming"] == 0
+    # the bound is strict: exactly 256 MB stays cached, one block more streams
+    per_pos = 8 * 128 * 2 * 2
+    nb = (256 << 20) // (per_pos * 16)
+    assert pa.plan(dims_of(gqa, num_blocks=nb), 0, 8, 16)["streaming"] == 0
+    assert pa.plan(dims_of(gqa, num_blocks=nb + 1), 0, 8, 16)["streaming"] == 1
+    long = workloads.WORKLOADS["long_splitk_bf16"]   # 131072 x 512 B = 64 MiB
+    assert pa.plan(dims_of(long, num_blocks=10240), 0, 1, 16)["streaming"] == 0
+    assert pa.plan(dims_of(long, num_blocks=10240), 0, 1, 16,
+                   loads=pa.LOADS_STREAMING)["streaming"] == 1
+    swa = workloads.WORKLOADS["swa_mtp_bf16"]        # the window bounds the span
+    assert pa.plan(dims_of(swa), 128, 8, 64)["streaming"] == 0
+    big = workloads.WORKLOADS["large_block_mtp_bf16"]
+    assert pa.plan(dims_of(big), 4096, 8, 1024)["streaming"] == 1
+    tiny = workloads.WORKLOADS["tiny_f32"]           # vector path: always cached
+    assert pa.plan(dims_of(tiny), 0, 1, 16, loads=pa.LOADS_STREAMING)["streaming"] == 0
 
 
 def test_plan_rejects_mfma_for_fp32(lib):

@@ -192,3 +192,24 @@ def test_peaked_logits(name, window):
     seqs = list(range(min(w.batch, 8)))
     exp, rows = oracle_out(c, seqs)
     compare(out, exp, rows, BF16_TOL, f"{name} peaked")
+
+
+@pytest.mark.parametrize("sched", [pa.SCHED_GRID, pa.SCHED_PERSISTENT])
+def test_load_forms_agree_bit_for_bit(sched):
+    """Non-temporal and cached KV loads fetch the same bytes into the same
+    registers: the outputs must be identical, on small MTP/window shapes and
+    on the GQA workload (whose plan picks the non-temporal form itself)."""
+    for win in (0, 5, 40):
+        w = mtp_workload(seq_lens=(150, 77, 33), batch=3, query_len=2)
+        c = workloads.make_case(w, device="cuda", window=win)
+        for P in (0, 32):
+            a = run_gpu(c, path=pa.PATH_MFMA, part_size=P, schedule=sched,
+                        loads=pa.LOADS_CACHED).clone()
+            b = run_gpu(c, path=pa.PATH_MFMA, part_size=P, schedule=sched,
+                        loads=pa.LOADS_STREAMING)
+            assert torch.equal(a, b), (sched, win, P)
+    w = workloads.WORKLOADS["gqa_bf16"]
+    c = workloads.make_case(w, device="cuda")
+    a = run_gpu(c, schedule=sched, loads=pa.LOADS_CACHED).clone()
+    assert torch.equal(run_gpu(c, schedule=sched), a)
+    say(f"[loads] schedule={sched}: cached and non-temporal outputs identical")
