@@ -10,7 +10,8 @@ fails, an exception says so.
               scale, window, num_kv_heads, block_size, max_seq_len=...)
 
 Layouts (see include/pa_decode.h): q/out [T, H_q, D]; k_cache
-[num_blocks, H_kv, block_size, D]; v_cache [num_blocks, H_kv, block_size/8, D, 8];
+[num_blocks, H_kv, block_size/16, 2, D/8, 8, 8] (16-slot tiles); v_cache
+[num_blocks, H_kv, block_size/8, D, 8] (8-slot tiles);
 block_tables int32 [B, max_blocks_per_seq]; seq_lens, query_lens int32 [B].
 """
 
@@ -196,8 +197,10 @@ def _validate(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, num_
         raise PaError(ERR_INVALID_ARG, "q and out must be [T, H_q, D] of one shape")
     T, Hq, D = q.shape
     nb = k_cache.shape[0]
-    if tuple(k_cache.shape) != (nb, num_kv_heads, block_size, D):
-        raise PaError(ERR_INVALID_ARG, f"k_cache must be [num_blocks, {num_kv_heads}, {block_size}, {D}]")
+    if block_size % 16 or D % 8 or tuple(k_cache.shape) != (nb, num_kv_heads, block_size // 16, 2,
+                                                             D // 8, 8, 8):
+        raise PaError(ERR_INVALID_ARG, f"k_cache must be [num_blocks, {num_kv_heads}, "
+                                       f"{block_size // 16}, 2, {D // 8}, 8, 8] (16-slot tiles)")
     if block_size % 8 or tuple(v_cache.shape) != (nb, num_kv_heads, block_size // 8, D, 8):
         raise PaError(ERR_INVALID_ARG, f"v_cache must be [num_blocks, {num_kv_heads}, "
                                        f"{block_size // 8}, {D}, 8]")

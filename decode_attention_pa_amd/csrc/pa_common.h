@@ -65,6 +65,16 @@ __device__ inline int phys_block(const int32_t* __restrict__ table_row, int t, i
   return table_row[t >> log2_bs];
 }
 
+// K cache slab of one (block, KV head): slots in groups of 16, each group a
+// [2][D/8][8][8] tile.  Half 0 holds slots 0-3 and 8-11, half 1 slots 4-7
+// and 12-15 (the positions one 16-row matrix-core K tile takes from a group);
+// in a half, column c (dims 8c .. 8c+7) stores its 8 slots one after another.
+// Element offset of (slot, dim 0); dim d adds (d >> 3) * 64 + (d & 7).
+__host__ __device__ inline int k_slot_offset(int slot, int D) {
+  const int u = slot & 15;
+  return (slot >> 4) * (16 * D) + ((u >> 2) & 1) * (8 * D) + ((u & 3) | ((u >> 3) << 2)) * 8;
+}
+
 // Exclusive prefix sum of query_lens[0 .. b) computed by one wave; every lane
 // returns the sum.  Gives the first q/out row of sequence b in the packed
 // [sum q_b, H_q, D] layout.

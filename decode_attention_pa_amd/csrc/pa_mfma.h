@@ -134,7 +134,9 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
     return cb;
   };
   // K rows: lane (ln, lg) of tile t holds position 8*(ln/4) + 4*t + ln%4 of
-  // the chunk, dims 8*lg + 32*s .. +7 for k-step s.
+  // the chunk, dims 8*lg + 32*s .. +7 for k-step s.  In the tiled K layout
+  // these are place ln%8 of half t of 16-slot group ln/8, column 4*s + lg:
+  // each load instruction reads two runs of 512 contiguous bytes.
   auto load_k = [&](int k, const ChunkBlocks& cb, u32x4 (&kr)[2][KS]) {
     const int cs = cb0 + k * kChunk;
 #pragma unroll
@@ -142,10 +144,10 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
       int pos = cs + 8 * (ln >> 2) + 4 * t + (ln & 3);
       pos = min(max(pos, ps), pe - 1);  // clamp: never touch blocks outside the span
       const int blk = (pos >> log2_bs) == cb.first_idx ? cb.first : cb.second;
-      const uint16_t* kp =
-          kc + (size_t)blk * blk_stride + head_off + (size_t)(pos & bs_mask) * D + lg * 8;
+      const uint16_t* kp = kc + (size_t)blk * blk_stride + head_off +
+                           k_slot_offset(pos & bs_mask, D) + lg * 64;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) kr[t][s] = ld_kv<STREAM>(kp + s * 32);
+      for (int s = 0; s < KS; ++s) kr[t][s] = ld_kv<STREAM>(kp + s * 256);
     }
   };
   // V^T columns: lane (ln, lg) holds dim 16*dt + ln, positions 8*lg .. +7.

@@ -5,8 +5,8 @@
 // context partition of one (sequence, KV head); its G*q_b <= 64 packed rows
 // (row n = i*G + g) share every K/V chunk, which is staged through LDS:
 //
-//   stage   K chunk [32][D] and V chunk [D][32] in fp32 (V read from its
-//           8-slot [D][8] tiles), positions outside
+//   stage   K chunk [32][D] and V chunk [D][32] in fp32 (K read from its
+//           16-slot tiles, V from its 8-slot [D][8] tiles), positions outside
 //           the partition stored as zeros (never read from HBM)
 //   scores  one thread per (row, position): D-term dot product, masked by
 //           select to -inf outside the row's visible interval
@@ -105,14 +105,15 @@ __global__ __launch_bounds__(256) void part_valu(PartArgs a) {
     const int cs = cb0 + k * kChunk;
     __syncthreads();  // previous chunk's readers are done
     {
-      // K: thread -> (position r, dims dsl, dsl+8, ...): coalesced along D.
+      // K: thread -> (position r, dims dsl, dsl+8, ...): the 8 threads of a
+      // position read 8 consecutive elements of each column of its slot.
       const int r = tid >> 3, dsl = tid & 7;
       const int pos = cs + r;
       const bool ok = pos >= ps && pos < pe;
       const T* kp = nullptr;
       if (ok) kp = kc + (size_t)phys_block(table, pos, log2_bs) * blk_stride + head_off +
-                   (size_t)(pos & bs_mask) * D;
-      for (int d = dsl; d < D; d += 8) k_s[r][d] = ok ? load_elem<T>(kp + d) : 0.f;
+                   k_slot_offset(pos & bs_mask, D) + dsl;
+      for (int d = dsl; d < D; d += 8) k_s[r][d] = ok ? load_elem<T>(kp + (d >> 3) * 64) : 0.f;
     }
     {
       // V: thread -> (position r, dims vd, vd+8, ...): coalesced along positions.

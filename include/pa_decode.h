@@ -28,7 +28,13 @@
  * Memory layouts (row-major, contiguous, all device memory):
  *   q, out        [T, H_q, D], T = sum_b q_b; sequence b owns rows
  *                 qoff_b .. qoff_b + q_b - 1, qoff_b = q_0 + ... + q_{b-1}
- *   k_cache       [num_blocks, H_kv, block_size, D]    (one row per position)
+ *   k_cache       [num_blocks, H_kv, block_size/16, 2, D/8, 8, 8]: slots grouped
+ *                 by 16; slot s of a group lives in half (s >> 2) & 1 at place
+ *                 (s & 3) | ((s >> 3) << 2), i.e. half 0 holds slots 0-3 and
+ *                 8-11, half 1 slots 4-7 and 12-15; each half is a [D/8][8][8]
+ *                 tile (8-dim column, place, dim within the column), so 16
+ *                 contiguous bytes hold 8 dims of one slot and a column of a
+ *                 half is 128 contiguous bytes
  *   v_cache       [num_blocks, H_kv, block_size/8, D, 8]: slots grouped by 8;
  *                 slot s of a block lives at [s/8][d][s%8] (a [D, 8] tile per
  *                 group: 16 contiguous bytes hold one dim of 8 consecutive

@@ -47,7 +47,7 @@ def brute_decode(q, k_cache, v_cache, block_tables, seq_lens, query_lens,
                     off = t % block_size
                     dot = 0.0
                     for d in range(D):
-                        dot += float(q[row][hq][d]) * float(k_cache[phys][kvh][off][d])
+                        dot += float(q[row][hq][d]) * _key(k_cache, phys, kvh, off, d)
                     logits.append(sigma * dot)
                     where.append((phys, off))
                 top = max(logits)
@@ -62,6 +62,25 @@ def brute_decode(q, k_cache, v_cache, block_tables, seq_lens, query_lens,
             out.append(out_row)
             row += 1
     return out
+
+
+def _key(k_cache, phys, kvh, off, d):
+    """Element d of slot ``off``'s key: a row per slot, or the tiled form
+    (16-slot groups; slots 0-3 and 8-11 in half 0, 4-7 and 12-15 in half 1,
+    dims in columns of 8)."""
+    slab = k_cache[phys][kvh]
+    if len(slab) and not hasattr(slab[0][0], "__len__"):     # [bs][D]
+        return float(slab[off][d])
+    grp, u = divmod(off, 16)
+    if u < 4:
+        half, place = 0, u
+    elif u < 8:
+        half, place = 1, u - 4
+    elif u < 12:
+        half, place = 0, u - 4
+    else:
+        half, place = 1, u - 8
+    return float(slab[grp][half][d // 8][place][d % 8])
 
 
 def _to_f32(x):

@@ -7,7 +7,11 @@ dtype; they are widened to float64 exactly), in the layouts the library uses:
     q            [T, H_q, D]          T = sum(query_lens); sequence b owns rows
                                       qoff_b .. qoff_b + query_lens[b] - 1,
                                       qoff_b = query_lens[0] + ... + query_lens[b-1]
-    k_cache      [num_blocks, H_kv, block_size, D]   (row per position)
+    k_cache      [num_blocks, H_kv, block_size, D]   (row per position), or
+                 the library's tiled form [num_blocks, H_kv, block_size/16, 2,
+                 D/8, 8, 8]: within each group of 16 slots, slot s lies in
+                 half (s // 4) % 2 at place s % 4 + 4 * (s // 8), and its dim d
+                 at column d // 8, lane d % 8 of that place
     v_cache      [num_blocks, H_kv, block_size/g, D, g]   (positions grouped by
                  g: for each group of g consecutive slots, a [D, g] tile; the
                  library uses g = 8, tests with blocks smaller than 8 use g = bs)
@@ -70,10 +74,18 @@ def check_args(q, block_tables, seq_lens, query_lens, num_kv_heads, block_size, 
 
 
 def gather_keys(k_cache, table_row, positions, h, block_size):
-    """K rows of positions t: k_cache[table[t // bs], h, t % bs, :] -> [n, D]."""
+    """K rows of positions t (slot s = t % bs of block table[t // bs]) -> [n, D]."""
     blocks = table_row[positions // block_size]
     offs = positions % block_size
-    return k_cache[blocks, h, offs, :].astype(np.float64)
+    if k_cache.ndim == 4:
+        return k_cache[blocks, h, offs, :].astype(np.float64)
+    n = len(positions)
+    grp, u = offs // 16, offs % 16
+    half = (u // 4) % 2
+    place = u % 4 + 4 * (u // 8)
+    tiles = k_cache[blocks, h, grp, half]                    # [n, D/8, 8 places, 8]
+    cols = tiles[np.arange(n), :, place, :]                  # [n, D/8, 8]
+    return cols.reshape(n, k_cache.shape[4] * k_cache.shape[6]).astype(np.float64)
 
 
 def gather_values(v_cache, table_row, positions, h, block_size):

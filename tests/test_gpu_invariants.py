@@ -106,7 +106,8 @@ def test_spike_probe_visibility(path, sched, window):
                     h = 0
                     qv = c.q[row, h].float()
                     alpha = 400.0 / (w.scale * float(qv.dot(qv)))
-                    c.k_cache[blk, h, t % bs, :] = (alpha * qv).to(torch.bfloat16)
+                    workloads.write_k_row(c.k_cache, blk, h, t % bs,
+                                          (alpha * qv).to(torch.bfloat16))
                     out = run_gpu(c, path=path, part_size=P, schedule=sched)
                     if lo_i <= t <= p_i:
                         expect = v_at(c, blk, h, t % bs)

@@ -84,6 +84,34 @@ def test_tiny_workload_matches_brute_force(window):
     assert np.max(np.abs(ref - bf)) <= 1e-12
 
 
+def _k_rows(k):
+    """Any K cache as rows [num_blocks, H_kv, bs, D]: the tiled form
+    (16-slot groups, two halves of 8 places, dims in columns of 8) undone
+    slot by slot."""
+    if k.ndim == 4:
+        return k
+    nb, H, ngrp, _, ncol, _, _ = k.shape
+    rows = np.empty((nb, H, ngrp * 16, ncol * 8), k.dtype)
+    for s in range(ngrp * 16):
+        u = s % 16
+        half = 1 if u % 8 >= 4 else 0
+        place = u % 4 + (4 if u >= 8 else 0)
+        rows[:, :, s, :] = k[:, :, s // 16, half, :, place, :].reshape(nb, H, ncol * 8)
+    return rows
+
+
+def _k_tiled(rows):
+    """Rows [num_blocks, H_kv, bs, D] into the tiled form, slot by slot."""
+    nb, H, bs, D = rows.shape
+    k = np.full((nb, H, bs // 16, 2, D // 8, 8, 8), np.nan)
+    for s in range(bs):
+        u = s % 16
+        half = 1 if u % 8 >= 4 else 0
+        place = u % 4 + (4 if u >= 8 else 0)
+        k[:, :, s // 16, half, :, place, :] = rows[:, :, s, :].reshape(nb, H, D // 8, 8)
+    return k
+
+
 def _sdpa_reference(a):
     """Gather each sequence's context contiguously and call torch SDPA (float64)."""
     out = []
@@ -94,7 +122,7 @@ def _sdpa_reference(a):
         L, ql = int(L), int(ql)
         t = np.arange(L)
         blk = a["block_tables"][b][t // bs]
-        K = a["k_cache"][blk, :, t % bs, :]                    # [L, Hkv, D]
+        K = _k_rows(a["k_cache"])[blk, :, t % bs, :]           # [L, Hkv, D]
         g = a["v_cache"].shape[-1]
         V = np.stack([a["v_cache"][blk[j], :, (t[j] % bs) // g, :, (t[j] % bs) % g]
                       for j in range(L)])                      # [L, Hkv, D]
@@ -120,6 +148,41 @@ def test_matches_torch_sdpa(seed):
     for win in windows_for(w.seq_lens):
         a = as_np(workloads.make_case(w, window=win, poison=False))
         assert np.max(np.abs(pa.decode(**a) - _sdpa_reference(a))) <= 1e-12
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_tiled_key_layout_is_the_row_layout(seed):
+    """The library's tiled K form holds the same keys as one row per slot:
+    converting a row-layout cache slot by slot gives identical oracle and
+    brute-force outputs, and the generator's tiled caches read back as rows
+    agree with the oracle's own gather."""
+    r = np.random.default_rng(300 + seed)
+    bs = int(r.choice([16, 32]))
+    w = tiny_random(seed + 70, block_size=bs, head_dim=int(r.choice([8, 16])),
+                    max_blocks_per_seq=-(-40 // bs) + 2)
+    for win in (0, 3):
+        a = as_np(workloads.make_case(w, window=win, poison=False))
+        assert a["k_cache"].ndim == 7                       # generator made the tiled form
+        rows = dict(a, k_cache=_k_rows(a["k_cache"]))
+        np.testing.assert_array_equal(pa.decode(**a), pa.decode(**rows))
+        np.testing.assert_array_equal(np.array(brute.brute_decode(**a)),
+                                      np.array(brute.brute_decode(**rows)))
+        back = dict(a, k_cache=_k_tiled(rows["k_cache"]))
+        np.testing.assert_array_equal(back["k_cache"], a["k_cache"])
+        # the generator's slot accessors agree with the slot-by-slot reading
+        kt = torch.from_numpy(a["k_cache"].copy())
+        for slot in range(bs):
+            np.testing.assert_array_equal(workloads.read_k_row(kt, 1, 0, slot).numpy(),
+                                          rows["k_cache"][1, 0, slot])
+            workloads.write_k_row(kt, 1, 0, slot, torch.full((kt.shape[4] * 8,), float(slot)))
+        assert np.all(_k_rows(kt.numpy())[1, 0] == np.arange(bs)[:, None])
+        for b in range(len(a["seq_lens"])):
+            t = np.arange(int(a["seq_lens"][b]))
+            blk = a["block_tables"][b][t // bs]
+            for h in range(a["num_kv_heads"]):
+                np.testing.assert_array_equal(
+                    pa.gather_keys(a["k_cache"], a["block_tables"][b], t, h, bs),
+                    rows["k_cache"][blk, h, t % bs, :])
 
 
 @pytest.mark.parametrize("window", [0, 5])

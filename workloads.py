@@ -6,7 +6,12 @@ can consume what it produces without sharing code.
 
 Layouts (the library's contract):
     q, out        [T, H_q, D], T = sum(query_lens), packed in sequence order
-    k_cache       [num_blocks, H_kv, block_size, D]
+    k_cache       [num_blocks, H_kv, block_size/16, 2, D/8, 8, 8]  (16-slot
+                  groups; slot s of a group sits in half (s >> 2) & 1, at
+                  place (s & 3) | ((s >> 3) << 2) of that half's [D/8][8][8]
+                  tile of 8-dim columns).  Shapes the library does not take
+                  (block_size < 16 or D not a multiple of 8, used only to pin
+                  the oracle) keep one row per slot: [num_blocks, H_kv, bs, D]
     v_cache       [num_blocks, H_kv, block_size/8, D, 8]  (8-slot groups, each a
                   [D, 8] tile; blocks smaller than 8 use one group of bs)
     block_tables  int32 [B, max_blocks_per_seq]
@@ -90,6 +95,34 @@ WORKLOADS = {
         description="large-block mixed-window MTP decode bf16: B=128, 64/8 heads, "
                     "D=128, bs=1024, context U[2048, 65536], q_len 2, window 4096 / 0"),
 }
+
+
+def k_tiled(block_size: int, head_dim: int) -> bool:
+    """True when the K cache takes the 16-slot tiled layout."""
+    return block_size % 16 == 0 and head_dim % 8 == 0
+
+
+def k_slot(slot):
+    """(group, half, place) of block slot(s) ``slot`` in the tiled K layout."""
+    u = slot % 16
+    return slot // 16, (u // 4) % 2, u % 4 + 4 * (u // 8)
+
+
+def read_k_row(k_cache, blk, h, slot):
+    """Copy of the D elements of one slot's key, for either K layout."""
+    if k_cache.dim() == 4:
+        return k_cache[blk, h, slot].clone()
+    c, half, j = k_slot(slot)
+    return k_cache[blk, h, c, half, :, j, :].reshape(-1).clone()
+
+
+def write_k_row(k_cache, blk, h, slot, row):
+    """Stores the D-vector ``row`` as the key of one slot, for either K layout."""
+    if k_cache.dim() == 4:
+        k_cache[blk, h, slot] = row
+    else:
+        c, half, j = k_slot(slot)
+        k_cache[blk, h, c, half, :, j, :] = row.reshape(-1, 8)
 
 
 def torch_dtype(name: str) -> torch.dtype:
@@ -189,7 +222,11 @@ def make_case(w: Workload | str, device="cpu", window: int | None = None,
     _fill_normal(q, vg)
     if q_gain != 1.0:
         q.copy_((q.float() * q_gain).to(dt))
-    k = torch.empty((pool, w.num_kv_heads, bs, w.head_dim), dtype=dt, device=dev)
+    D = w.head_dim
+    tiled = k_tiled(bs, D)
+    kshape = (pool, w.num_kv_heads, bs // 16, 2, D // 8, 8, 8) if tiled else \
+        (pool, w.num_kv_heads, bs, D)
+    k = torch.empty(kshape, dtype=dt, device=dev)
     g = min(8, bs)
     v = torch.empty((pool, w.num_kv_heads, bs // g, w.head_dim, g), dtype=dt, device=dev)
     _fill_normal(k, vg)
@@ -203,8 +240,12 @@ def make_case(w: Workload | str, device="cpu", window: int | None = None,
             tail = L % bs
             if tail and used[b]:
                 last = used[b][-1]
-                k[last, :, tail:, :] = float("nan")
                 slots = torch.arange(tail, bs, device=dev)
+                if tiled:
+                    c, half, j = k_slot(slots)
+                    k[last, :, c, half, :, j, :] = float("nan")
+                else:
+                    k[last, :, tail:, :] = float("nan")
                 v[last, :, slots // g, :, slots % g] = float("nan")
     return Case(
         w=w, window=int(window), q=q, k_cache=k, v_cache=v,
