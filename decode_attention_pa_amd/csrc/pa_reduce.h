@@ -21,7 +21,7 @@ namespace pa {
 // one (sequence, KV head); the GP threads of a group split the partitions
 // (GP = 1, 16 or 256, chosen on the host from NP) and combine their partial
 // sums by a fixed butterfly / tree, so results are deterministic.  Each
-// thread requests all of its partitions' float4 slices before using them.
+// thread requests all of its partitions' states before using them.
 // Grid: x = unit blocks of 256/GP units, y = KV head, z = sequence.
 template <int GP>
 struct GroupReduce {
@@ -69,15 +69,16 @@ __global__ __launch_bounds__(256) void lse_reduce(ReduceArgs a) {
   __shared__ float lds[4];
   const int h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
+  // One round of independent loads: lengths, run count, row offset.
   const int L = a.seq_lens[b];
   const int q = a.query_lens[b];
+  const int runs = a.ws_runs ? a.ws_runs[(size_t)b * a.num_kv_heads + h] : 0;
+  const int qoff = wave_row_offset(a.query_lens, b);  // all lanes still active
   const int G = a.group;
   const SeqView sv = seq_view(L, q, a.window, a.part_size);
   // states to merge: one per partition, or the unit's run count
-  const int np = a.ws_runs ? min(a.ws_runs[(size_t)b * a.num_kv_heads + h], a.num_parts)
-                           : (sv.nparts > 1 ? min(sv.nparts, a.num_parts) : 0);
+  const int np = a.ws_runs ? min(runs, a.num_parts) : (sv.nparts > 1 ? min(sv.nparts, a.num_parts) : 0);
   if (np <= 0) return;  // the partition kernel wrote these rows directly
-  const int qoff = wave_row_offset(a.query_lens, b);  // all lanes still active
   const int unit = blockIdx.x * UPW + tid / GP;
   const int gp = tid % GP;
   const int n = unit / D4, d4 = unit % D4;
@@ -91,21 +92,20 @@ __global__ __launch_bounds__(256) void lse_reduce(ReduceArgs a) {
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
   for (int j0 = gp; j0 < np; j0 += GP * U) {
-    // states first; partial outputs only for slots where the row saw
-    // something (max > -inf)
+    // Every slot below np was written by this call's partition kernel, with
+    // finite values (a row that saw nothing stores m = -inf, l = 0, o = 0),
+    // so all three are requested together: one round trip per step.
     float mj[U], lj[U];
     f32x4 o[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int jj = j0 + u * GP;
-      mj[u] = jj < np ? a.ws_m[(base + jj) * a.rows + n] : -INFINITY;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
+      mj[u] = -INFINITY;
       lj[u] = 0.f;
       o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (mj[u] != -INFINITY) {
-        const size_t w = (base + j0 + u * GP) * a.rows + n;
+      if (jj < np) {
+        const size_t w = (base + jj) * a.rows + n;
+        mj[u] = a.ws_m[w];
         lj[u] = a.ws_l[w];
         o[u] = *(const f32x4*)(a.ws_o + w * D + d4 * 4);
       }
