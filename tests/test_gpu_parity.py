@@ -230,3 +230,66 @@ def test_reduce_lane_modes(P, sched):
         exp, rows = oracle_out(c)
         compare(run_gpu(c, part_size=P, schedule=sched), exp, rows, BF16_TOL,
                 f"reduce P={P} sched={sched} w={win}")
+
+
+def _case_for_reuse():
+    return workloads.make_case(small(21, head_dim=128, num_q_heads=16, num_kv_heads=2, query_len=2,
+                                     batch=3, seq_lens=(9000, 3000, 129), block_size=32,
+                                     max_seq_len=9000, max_blocks_per_seq=283), device="cuda")
+
+
+REUSE_PLANS = [dict(part_size=32, schedule=pa.SCHED_GRID),      # 283 partitions: 256-lane merge
+               dict(part_size=256, schedule=pa.SCHED_GRID),     # 36 partitions: 16-lane merge
+               dict(part_size=512, schedule=pa.SCHED_PERSISTENT),
+               dict(schedule=pa.SCHED_PERSISTENT),
+               dict(path=pa.PATH_VALU, part_size=64)]
+
+
+def test_workspace_contents_do_not_matter():
+    """Every workspace byte a call reads was written by the same call: a
+    workspace full of random bytes, or left behind by calls with other plans,
+    gives the same output bits as a zeroed one."""
+    c = _case_for_reuse()
+    dims = pa.dims_for(c.q, c.k_cache, c.block_tables, 2, c.w.max_seq_len)
+    need = max(pa.workspace_size(dims, 0, 2, 32, **o) for o in REUSE_PLANS)
+    ref_out = []
+    for o in REUSE_PLANS:
+        ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+        ref_out.append(run_gpu(c, workspace=ws, **o).clone())
+    g = torch.Generator(device="cuda").manual_seed(5)
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda", generator=g)
+    for rep in range(2):
+        for o, expect in zip(REUSE_PLANS, ref_out):
+            assert torch.equal(run_gpu(c, workspace=ws, **o), expect), (rep, o)
+    say("[workspace] random and reused workspaces: identical outputs")
+
+
+def test_graph_replays_match_eager():
+    """A captured call (partition kernel + merge kernel) replays to the eager
+    result every time, with eager calls on the same workspace in between."""
+    c = _case_for_reuse()
+    dims = pa.dims_for(c.q, c.k_cache, c.block_tables, 2, c.w.max_seq_len)
+    for o in REUSE_PLANS[:2] + REUSE_PLANS[3:4]:
+        ws = torch.zeros(pa.workspace_size(dims, 0, 2, 32, **o), dtype=torch.uint8, device="cuda")
+        eager = run_gpu(c, workspace=ws, **o).clone()
+        out_g = torch.full_like(eager, float("nan"))
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            pa.decode(out_g, c.q, c.k_cache, c.v_cache, c.block_tables, c.seq_lens, c.query_lens,
+                      c.scale, c.window, c.w.num_kv_heads, c.w.block_size,
+                      max_seq_len=c.w.max_seq_len, max_query_len=2, workspace=ws, **o)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            pa.decode(out_g, c.q, c.k_cache, c.v_cache, c.block_tables, c.seq_lens, c.query_lens,
+                      c.scale, c.window, c.w.num_kv_heads, c.w.block_size,
+                      max_seq_len=c.w.max_seq_len, max_query_len=2, workspace=ws, **o)
+        for rep in range(3):
+            out_g.fill_(float("nan"))
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out_g, eager), (o, rep)
+            assert torch.equal(run_gpu(c, workspace=ws, **o), eager), (o, rep)
+        say(f"[graph] {o}: 3 replays identical to eager")
