@@ -33,8 +33,13 @@ What is computed, and where it comes from:
   the visibility predicate tested per position; written independently of the
   range arithmetic in ``paged_attention``.
 
-Readings of points the pages leave open are listed in the design doc and restated
-where they are used.  Every function here is pinned by ``tests/test_oracle*.py``
+* ``paged_attention.decode_e4m3`` / ``dequantize`` — FP8 (OCP E4M3) cache
+  codes to values, times the per-tensor key / value scale (aiter PR #2914,
+  review of ``pa_decode_gluon``: FP8 caches come with key_scale /
+  value_scale); ``brute.e4m3_value`` decodes one code bit field by bit field.
+
+Readings of points the pages leave open are restated where they are used.
+Every function here is pinned by ``tests/test_oracle*.py``
 to something other than itself (brute force, a textbook library routine,
 closed forms, invariants, hand-derived fixtures under ``tests/golden/``).
 """

@@ -67,10 +67,11 @@ def brute_decode(q, k_cache, v_cache, block_tables, seq_lens, query_lens,
 def _key(k_cache, phys, kvh, off, d):
     """Element d of slot ``off``'s key: a row per slot, or the tiled form
     (16-slot groups; slots 0-3 and 8-11 in half 0, 4-7 and 12-15 in half 1,
-    dims in columns of 8)."""
+    dims in columns of 8 for bf16 or 16 for FP8)."""
     slab = k_cache[phys][kvh]
     if len(slab) and not hasattr(slab[0][0], "__len__"):     # [bs][D]
         return float(slab[off][d])
+    width = len(slab[0][0][0][0])                           # dims per column
     grp, u = divmod(off, 16)
     if u < 4:
         half, place = 0, u
@@ -80,9 +81,21 @@ def _key(k_cache, phys, kvh, off, d):
         half, place = 0, u - 4
     else:
         half, place = 1, u - 8
-    return float(slab[grp][half][d // 8][place][d % 8])
+    return float(slab[grp][half][d // width][place][d % width])
 
 
 def _to_f32(x):
     import struct
     return struct.unpack("f", struct.pack("f", float(x)))[0]
+
+
+def e4m3_value(code):
+    """One OCP E4M3 code as a Python float, bit field by bit field."""
+    sign = -1.0 if code & 0x80 else 1.0
+    exponent = (code >> 3) & 0xF
+    mantissa = code & 0x7
+    if exponent == 0xF and mantissa == 0x7:
+        return math.nan
+    if exponent == 0:
+        return sign * mantissa * 2.0 ** -9           # subnormal: (m / 8) * 2^-6
+    return sign * (8 + mantissa) * 2.0 ** (exponent - 10)   # (1 + m / 8) * 2^(e - 7)

@@ -9,19 +9,24 @@ dtype; they are widened to float64 exactly), in the layouts the library uses:
                                       qoff_b = query_lens[0] + ... + query_lens[b-1]
     k_cache      [num_blocks, H_kv, block_size, D]   (row per position), or
                  the library's tiled form [num_blocks, H_kv, block_size/16, 2,
-                 D/8, 8, 8]: within each group of 16 slots, slot s lies in
-                 half (s // 4) % 2 at place s % 4 + 4 * (s // 8), and its dim d
-                 at column d // 8, lane d % 8 of that place
+                 D/E, 8, E] (E = 8 for bf16, 16 for FP8): within each group of
+                 16 slots, slot s lies in half (s // 4) % 2 at place
+                 s % 4 + 4 * (s // 8), and its dim d at column d // E,
+                 element d % E of that place
     v_cache      [num_blocks, H_kv, block_size/g, D, g]   (positions grouped by
                  g: for each group of g consecutive slots, a [D, g] tile; the
-                 library uses g = 8, tests with blocks smaller than 8 use g = bs)
+                 library uses g = 8 for bf16 and g = 16 for FP8, tests with
+                 blocks smaller than 8 use g = bs)
     block_tables [B, max_blocks_per_seq] int
     seq_lens     [B] int   context length, the query tokens included
     query_lens   [B] int   trailing query tokens of each context
 
 The cache layouts are a reading: the pages name a paged KV cache with a block
 size (aiter PR #2914 summary: "KV_BLOCK_SIZE=1024 path") but never its
-physical layout.
+physical layout.  FP8 caches use the same tiled forms with 16 one-byte
+elements where bf16 has 8 two-byte ones (K columns of 16 dims, V groups of 16
+slots); ``dequantize`` turns their codes into values first, and the gathers
+below read the column and group widths from the array shapes.
 """
 
 from __future__ import annotations
@@ -29,6 +34,27 @@ from __future__ import annotations
 import math
 
 import numpy as np
+
+
+def decode_e4m3(codes):
+    """Values of 8-bit floating-point codes in the OCP E4M3 format: sign bit,
+    4 exponent bits (bias 7), 3 mantissa bits; exponent 0 holds the
+    subnormals m/8 * 2^-6; the code with all exponent and mantissa bits set is
+    NaN; there are no infinities.  Returns float64 (exact)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    val = sign * val
+    return np.where((c & 0x7F) == 0x7F, np.nan, val)
+
+
+def dequantize(codes, scale):
+    """An FP8 cache as float64 values: code value times the per-tensor scale
+    (aiter PR #2914, review of ``pa_decode_gluon``: FP8 key and value caches
+    come with key_scale / value_scale).  The layout is kept."""
+    return decode_e4m3(codes) * float(np.float32(scale))
 
 
 def row_position(seq_len: int, query_len: int, i: int) -> int:

@@ -29,11 +29,18 @@ from oracle import paged_attention as pa
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
+def _values(cache, scale):
+    """Cache tensor as float64 values (FP8 codes dequantized by the oracle)."""
+    if cache.dtype == torch.float8_e4m3fn:
+        return pa.dequantize(cache.view(torch.uint8).numpy(), scale)
+    return cache.float().numpy().astype(np.float64)
+
+
 def as_np(case):
     return dict(
         q=case.q.float().numpy().astype(np.float64),
-        k_cache=case.k_cache.float().numpy().astype(np.float64),
-        v_cache=case.v_cache.float().numpy().astype(np.float64),
+        k_cache=_values(case.k_cache, case.w.k_scale),
+        v_cache=_values(case.v_cache, case.w.v_scale),
         block_tables=case.block_tables.numpy().astype(np.int64),
         seq_lens=np.array(case.seq_lens_host), query_lens=np.array(case.query_lens_host),
         scale=case.scale, window=case.window,
@@ -86,17 +93,17 @@ def test_tiny_workload_matches_brute_force(window):
 
 def _k_rows(k):
     """Any K cache as rows [num_blocks, H_kv, bs, D]: the tiled form
-    (16-slot groups, two halves of 8 places, dims in columns of 8) undone
-    slot by slot."""
+    (16-slot groups, two halves of 8 places, dims in columns of 8 or 16)
+    undone slot by slot."""
     if k.ndim == 4:
         return k
-    nb, H, ngrp, _, ncol, _, _ = k.shape
-    rows = np.empty((nb, H, ngrp * 16, ncol * 8), k.dtype)
+    nb, H, ngrp, _, ncol, _, width = k.shape
+    rows = np.empty((nb, H, ngrp * 16, ncol * width), k.dtype)
     for s in range(ngrp * 16):
         u = s % 16
         half = 1 if u % 8 >= 4 else 0
         place = u % 4 + (4 if u >= 8 else 0)
-        rows[:, :, s, :] = k[:, :, s // 16, half, :, place, :].reshape(nb, H, ncol * 8)
+        rows[:, :, s, :] = k[:, :, s // 16, half, :, place, :].reshape(nb, H, ncol * width)
     return rows
 
 
@@ -378,3 +385,46 @@ def test_poisoned_tail_and_unused_blocks_are_not_visible():
         a = as_np(workloads.make_case("tiny_f32", window=win, poison=True))
         assert np.isnan(a["k_cache"]).any()
         assert np.all(np.isfinite(pa.decode(**a)))
+
+
+
+def test_e4m3_decoding_matches_the_format():
+    """All 256 codes: the oracle's vectorised decoder, the brute-force bit-field
+    decoder and torch's float8_e4m3fn conversion agree (NaN for 0x7F / 0xFF);
+    and a few values fixed by the format: 448 is the largest finite value,
+    2^-6 the smallest normal, 2^-9 the smallest subnormal."""
+    codes = np.arange(256, dtype=np.uint8)
+    mine = pa.decode_e4m3(codes)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    bits = np.array([brute.e4m3_value(int(c)) for c in codes])
+    np.testing.assert_array_equal(mine, lib)
+    np.testing.assert_array_equal(mine, bits)
+    assert np.isnan(mine[0x7F]) and np.isnan(mine[0xFF]) and np.isfinite(mine[0x7E])
+    assert mine[0x7E] == 448.0 and mine[0xFE] == -448.0
+    assert mine[0x08] == 2.0 ** -6 and mine[0x01] == 2.0 ** -9 and mine[0x07] == 7 * 2.0 ** -9
+    assert mine[0x38] == 1.0 and mine[0xB8] == -1.0 and mine[0x00] == 0.0
+    assert np.nanmax(mine) == 448.0 and np.count_nonzero(np.isnan(mine)) == 2
+    # dequantize multiplies by the float32 value of the scale
+    assert pa.dequantize(np.array([0x38], np.uint8), 0.1)[0] == float(np.float32(0.1))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_fp8_caches_match_brute_force_and_rows(seed):
+    """FP8 tiled caches (K columns of 16 dims, V groups of 16 slots): the
+    oracle on dequantized codes equals the brute force, equals the oracle on
+    the same values laid out one row per slot, and equals torch SDPA."""
+    r = np.random.default_rng(400 + seed)
+    bs = int(r.choice([16, 32]))
+    w = tiny_random(seed + 90, block_size=bs, head_dim=int(r.choice([16, 32])), dtype="bf16",
+                    kv_dtype="fp8", max_blocks_per_seq=-(-40 // bs) + 2)
+    for win in (0, 4):
+        case = workloads.make_case(w, window=win, poison=False)
+        assert case.k_cache.dtype == torch.float8_e4m3fn and case.k_cache.shape[-1] == 16
+        a = as_np(case)
+        ref = pa.decode(**a)
+        assert np.max(np.abs(ref - np.array(brute.brute_decode(**a)))) <= 1e-12
+        rows = dict(a, k_cache=_k_rows(a["k_cache"]))
+        np.testing.assert_array_equal(ref, pa.decode(**rows))
+        assert np.max(np.abs(ref - _sdpa_reference(a))) <= 1e-12
+        # the cached values are the codes times the scales, not the codes
+        assert np.nanmax(np.abs(a["k_cache"])) <= 448 * float(np.float32(w.k_scale))

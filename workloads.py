@@ -14,6 +14,11 @@ Layouts (the library's contract):
                   the oracle) keep one row per slot: [num_blocks, H_kv, bs, D]
     v_cache       [num_blocks, H_kv, block_size/8, D, 8]  (8-slot groups, each a
                   [D, 8] tile; blocks smaller than 8 use one group of bs)
+    FP8 KV (kv_dtype "fp8"): OCP E4M3 codes (torch.float8_e4m3fn) with the same
+                  tiles at 16 one-byte elements per 16 bytes: k_cache
+                  [num_blocks, H_kv, bs/16, 2, D/16, 8, 16], v_cache
+                  [num_blocks, H_kv, bs/16, D, 16]; value = code * k_scale
+                  (v_scale), per-tensor float32 scales on the device
     block_tables  int32 [B, max_blocks_per_seq]
     seq_lens      int32 [B]  (context length, query tokens included)
     query_lens    int32 [B]
@@ -25,9 +30,11 @@ permutation of the pool is dealt out to the sequences in order.  Table
 entries past a sequence's last block point at an unused pool block.  Q, K and
 V are N(0, 1) drawn in float32 with a generator seeded from the same seed on
 the target device, then rounded to the workload dtype (round-to-nearest-
-even).  With ``poison=True`` every pool block no table uses, and every slot
-at or past seq_len in a sequence's last block, is filled with NaN, so any
-read of memory outside the context shows up in the output.
+even).  FP8 caches divide the N(0, 1) draws by the workload's scale, clamp
+to the format's +-448 and round to the nearest E4M3 code.  With
+``poison=True`` every pool block no table uses, and every slot at or past
+seq_len in a sequence's last block, is filled with NaN, so any read of
+memory outside the context shows up in the output.
 """
 
 from __future__ import annotations
@@ -58,6 +65,9 @@ class Workload:
     query_lens: tuple = ()     # per-sequence query lengths (default: query_len each)
     pool: int = 0              # physical blocks; 0 = ceil(1.25 x needed)
     description: str = ""
+    kv_dtype: str = ""         # "" = the workload dtype, "fp8" = OCP E4M3 codes + scales
+    k_scale: float = 0.0123    # FP8 only: K value = code * k_scale
+    v_scale: float = 0.0157    # FP8 only: V value = code * v_scale
 
 
 WORKLOADS = {
@@ -87,6 +97,14 @@ WORKLOADS = {
         max_seq_len=131072, seq_lens=(131072,), pool=10240,
         description="single-KV-group long-context split-K decode bf16: B=1, "
                     "8/1 heads, D=128, bs=16, context 131072, q_len 1, window 0"),
+    "gqa_fp8kv": Workload(
+        name="gqa_fp8kv", dtype="bf16", kv_dtype="fp8", batch=32, num_q_heads=32,
+        num_kv_heads=8, head_dim=128, block_size=16, query_len=1, windows=(0,),
+        scale=1.0 / math.sqrt(128.0), seed=2, max_blocks_per_seq=512,
+        max_seq_len=8192, len_range=(512, 8192),
+        description="GQA decode, bf16 queries over an FP8 (E4M3) KV cache with "
+                    "per-tensor scales: B=32, 32/8 heads, D=128, bs=16, "
+                    "context U[512, 8192], q_len 1, window 0"),
     "large_block_mtp_bf16": Workload(
         name="large_block_mtp_bf16", dtype="bf16", batch=128, num_q_heads=64,
         num_kv_heads=8, head_dim=128, block_size=1024, query_len=2, windows=(4096, 0),
@@ -97,9 +115,9 @@ WORKLOADS = {
 }
 
 
-def k_tiled(block_size: int, head_dim: int) -> bool:
+def k_tiled(block_size: int, head_dim: int, elem_bytes: int = 2) -> bool:
     """True when the K cache takes the 16-slot tiled layout."""
-    return block_size % 16 == 0 and head_dim % 8 == 0
+    return block_size % 16 == 0 and head_dim % (16 // elem_bytes) == 0
 
 
 def k_slot(slot):
@@ -117,12 +135,18 @@ def read_k_row(k_cache, blk, h, slot):
 
 
 def write_k_row(k_cache, blk, h, slot, row):
-    """Stores the D-vector ``row`` as the key of one slot, for either K layout."""
+    """Stores the D-vector ``row`` as the key of one slot, for either K layout
+    (``row`` already in the cache's element type)."""
     if k_cache.dim() == 4:
         k_cache[blk, h, slot] = row
     else:
         c, half, j = k_slot(slot)
-        k_cache[blk, h, c, half, :, j, :] = row.reshape(-1, 8)
+        k_cache[blk, h, c, half, :, j, :] = row.reshape(-1, k_cache.shape[-1])
+
+
+def to_e4m3(x: torch.Tensor, scale: float) -> torch.Tensor:
+    """Nearest OCP E4M3 codes of x / scale, saturated at +-448."""
+    return (x.float() / scale).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn)
 
 
 def torch_dtype(name: str) -> torch.dtype:
@@ -146,6 +170,8 @@ class Case:
     used_blocks: list           # per sequence, physical ids in logical order
     unused_blocks: list
     extra: dict = field(default_factory=dict)
+    k_scale: torch.Tensor | None = None   # FP8 caches: float32 [1] on the device
+    v_scale: torch.Tensor | None = None
 
     @property
     def scale(self) -> float:
@@ -223,36 +249,57 @@ def make_case(w: Workload | str, device="cpu", window: int | None = None,
     if q_gain != 1.0:
         q.copy_((q.float() * q_gain).to(dt))
     D = w.head_dim
-    tiled = k_tiled(bs, D)
-    kshape = (pool, w.num_kv_heads, bs // 16, 2, D // 8, 8, 8) if tiled else \
+    fp8 = w.kv_dtype == "fp8"
+    E = 16 if fp8 else 8                    # elements per 16-byte column / V group
+    tiled = k_tiled(bs, D, 1 if fp8 else 2)
+    kshape = (pool, w.num_kv_heads, bs // 16, 2, D // E, 8, E) if tiled else \
         (pool, w.num_kv_heads, bs, D)
-    k = torch.empty(kshape, dtype=dt, device=dev)
-    g = min(8, bs)
-    v = torch.empty((pool, w.num_kv_heads, bs // g, w.head_dim, g), dtype=dt, device=dev)
-    _fill_normal(k, vg)
-    _fill_normal(v, vg)
+    g = min(E, bs)
+    vshape = (pool, w.num_kv_heads, bs // g, w.head_dim, g)
+    if fp8:
+        k = torch.empty(kshape, dtype=torch.float32, device=dev)
+        v = torch.empty(vshape, dtype=torch.float32, device=dev)
+        _fill_normal(k, vg)
+        _fill_normal(v, vg)
+        k = to_e4m3(k, w.k_scale)
+        v = to_e4m3(v, w.v_scale)
+    else:
+        k = torch.empty(kshape, dtype=dt, device=dev)
+        v = torch.empty(vshape, dtype=dt, device=dev)
+        _fill_normal(k, vg)
+        _fill_normal(v, vg)
+    nan = float("nan")
     if poison:
         if unused:
             ids = torch.tensor(unused, dtype=torch.long, device=dev)
-            k.index_fill_(0, ids, float("nan"))
-            v.index_fill_(0, ids, float("nan"))
+            if fp8:   # E4M3 NaN code 0x7F in every byte
+                k.view(torch.uint8).index_fill_(0, ids, 0x7F)
+                v.view(torch.uint8).index_fill_(0, ids, 0x7F)
+            else:
+                k.index_fill_(0, ids, nan)
+                v.index_fill_(0, ids, nan)
         for b, L in enumerate(lens):
             tail = L % bs
             if tail and used[b]:
                 last = used[b][-1]
                 slots = torch.arange(tail, bs, device=dev)
+                kb = k.view(torch.uint8) if fp8 else k
+                vb = v.view(torch.uint8) if fp8 else v
+                bad = 0x7F if fp8 else nan
                 if tiled:
                     c, half, j = k_slot(slots)
-                    k[last, :, c, half, :, j, :] = float("nan")
+                    kb[last, :, c, half, :, j, :] = bad
                 else:
-                    k[last, :, tail:, :] = float("nan")
-                v[last, :, slots // g, :, slots % g] = float("nan")
+                    kb[last, :, tail:, :] = bad
+                vb[last, :, slots // g, :, slots % g] = bad
     return Case(
         w=w, window=int(window), q=q, k_cache=k, v_cache=v,
         block_tables=tables.to(dev), seq_lens=torch.tensor(lens, dtype=torch.int32, device=dev),
         query_lens=torch.tensor(qls, dtype=torch.int32, device=dev),
         seq_lens_host=lens, query_lens_host=qls, tables_host=tables,
-        used_blocks=used, unused_blocks=unused)
+        used_blocks=used, unused_blocks=unused,
+        k_scale=torch.tensor([w.k_scale], dtype=torch.float32, device=dev) if fp8 else None,
+        v_scale=torch.tensor([w.v_scale], dtype=torch.float32, device=dev) if fp8 else None)
 
 
 def custom(name="custom", **kw) -> Workload:
