@@ -52,6 +52,7 @@ def algorithmic_bytes(case) -> dict:
     """Bytes the method must move for one call (see module docstring)."""
     w = case.w
     s = 2 if w.dtype == "bf16" else 4
+    skv = 1 if w.kv_dtype == "fp8" else s      # bytes per cached K / V element
     kv = 0
     tables = 0
     bs = w.block_size
@@ -59,7 +60,7 @@ def algorithmic_bytes(case) -> dict:
         if q <= 0:
             continue
         lo = 0 if case.window == 0 else max(0, L - q + 1 - case.window)
-        kv += w.num_kv_heads * (L - lo) * w.head_dim * 2 * s
+        kv += w.num_kv_heads * (L - lo) * w.head_dim * 2 * skv
         tables += 4 * ((L - 1) // bs - lo // bs + 1)
     T = sum(case.query_lens_host)
     qb = T * w.num_q_heads * w.head_dim * s
@@ -220,7 +221,8 @@ def main(argv=None):
                        schedule={"auto": 0, "grid": pa.SCHED_GRID,
                                  "persistent": pa.SCHED_PERSISTENT}[a.schedule],
                        loads={"auto": 0, "cached": pa.LOADS_CACHED,
-                              "streaming": pa.LOADS_STREAMING}[a.loads])
+                              "streaming": pa.LOADS_STREAMING}[a.loads],
+                       k_scale=case.k_scale, v_scale=case.v_scale)
     # flush = reading 1 GiB evicts the workload from L2 and the 256 MB MALL
     # with clean lines (a write would leave dirty lines behind to write back)
     flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda") if a.flush else None
@@ -308,6 +310,7 @@ def main(argv=None):
             "workload": w.name, "description": w.description, "window": window,
             "batch": w.batch, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
             "head_dim": w.head_dim, "block_size": w.block_size, "query_len": w.query_len,
+            "kv_dtype": w.kv_dtype or w.dtype,
             "realised_context_tokens": sum(case.seq_lens_host), "plan": call.plan,
             "flush_between_calls": bool(a.flush),
         },

@@ -49,7 +49,8 @@ class Dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("max_query_len", ctypes.c_int32),
                 ("max_seq_len", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
-                ("num_blocks", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("num_blocks", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("kv_format", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):
@@ -67,7 +68,8 @@ class Options(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("part_size", ctypes.c_int32),
                 ("waves", ctypes.c_int32), ("schedule", ctypes.c_int32),
                 ("loads", ctypes.c_int32),
-                ("event_begin", ctypes.c_void_p), ("event_end", ctypes.c_void_p)]
+                ("event_begin", ctypes.c_void_p), ("event_end", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
 
 
 _lib = None
@@ -115,10 +117,14 @@ def _check(status: int):
                               f"{lib.pa_last_error().decode()}")
 
 
+KV_NATIVE, KV_FP8_E4M3 = 0, 1
+
+
 def make_dims(batch, num_q_heads, head_dim, max_query_len, max_seq_len, max_blocks_per_seq,
-              num_blocks, dtype) -> Dims:
+              num_blocks, dtype, kv_format=KV_NATIVE) -> Dims:
     return Dims(int(batch), int(num_q_heads), int(head_dim), int(max_query_len),
-                int(max_seq_len), int(max_blocks_per_seq), int(num_blocks), int(dtype))
+                int(max_seq_len), int(max_blocks_per_seq), int(num_blocks), int(dtype),
+                int(kv_format))
 
 
 SCHED_AUTO, SCHED_GRID, SCHED_PERSISTENT = 0, 1, 2
@@ -126,9 +132,21 @@ LOADS_AUTO, LOADS_CACHED, LOADS_STREAMING = 0, 1, 2
 
 
 def make_options(path=0, part_size=0, waves=0, event_begin=None, event_end=None,
-                 schedule=0, loads=0) -> Options:
+                 schedule=0, loads=0, k_scale=None, v_scale=None) -> Options:
     return Options(int(path), int(part_size), int(waves), int(schedule), int(loads),
-                   _event_handle(event_begin), _event_handle(event_end))
+                   _event_handle(event_begin), _event_handle(event_end),
+                   _scale_ptr(k_scale), _scale_ptr(v_scale))
+
+
+def _scale_ptr(t):
+    """Device pointer of a float32 scale tensor (one element), or None."""
+    if t is None:
+        return None
+    import torch
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype != torch.float32 \
+            or t.numel() != 1:
+        raise PaError(ERR_INVALID_ARG, "k_scale / v_scale must be float32 CUDA tensors of one element")
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _event_handle(ev):
@@ -171,10 +189,15 @@ def _stream_handle(stream):
     return ctypes.c_void_p(int(stream.cuda_stream))
 
 
+def _kv_format(k_cache) -> int:
+    import torch
+    return KV_FP8_E4M3 if k_cache.dtype == torch.float8_e4m3fn else KV_NATIVE
+
+
 def dims_for(q, k_cache, block_tables, max_query_len, max_seq_len) -> Dims:
     T, Hq, D = q.shape
     return make_dims(block_tables.shape[0], Hq, D, max_query_len, max_seq_len,
-                     block_tables.shape[1], k_cache.shape[0], _dtype_code(q))
+                     block_tables.shape[1], k_cache.shape[0], _dtype_code(q), _kv_format(k_cache))
 
 
 def _validate(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, num_kv_heads, block_size):
@@ -191,19 +214,26 @@ def _validate(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, num_
     for name, t in (("block_tables", block_tables), ("seq_lens", seq_lens), ("query_lens", query_lens)):
         if t.dtype != torch.int32:
             raise PaError(ERR_INVALID_ARG, f"{name} must be int32")
-    if not (q.dtype == k_cache.dtype == v_cache.dtype == out.dtype):
+    fp8 = k_cache.dtype == torch.float8_e4m3fn
+    if q.dtype != out.dtype:
+        raise PaError(ERR_INVALID_ARG, "q and out must share one dtype")
+    if fp8:
+        if v_cache.dtype != torch.float8_e4m3fn or q.dtype != torch.bfloat16:
+            raise PaError(ERR_INVALID_ARG, "an FP8 k_cache needs an FP8 v_cache and bf16 q / out")
+    elif not (q.dtype == k_cache.dtype == v_cache.dtype):
         raise PaError(ERR_INVALID_ARG, "q, k_cache, v_cache and out must share one dtype")
     if q.dim() != 3 or out.shape != q.shape:
         raise PaError(ERR_INVALID_ARG, "q and out must be [T, H_q, D] of one shape")
     T, Hq, D = q.shape
     nb = k_cache.shape[0]
-    if block_size % 16 or D % 8 or tuple(k_cache.shape) != (nb, num_kv_heads, block_size // 16, 2,
-                                                             D // 8, 8, 8):
+    E = 16 if fp8 else 8                     # elements per 16-byte column / V group
+    if block_size % 16 or D % E or tuple(k_cache.shape) != (nb, num_kv_heads, block_size // 16, 2,
+                                                             D // E, 8, E):
         raise PaError(ERR_INVALID_ARG, f"k_cache must be [num_blocks, {num_kv_heads}, "
-                                       f"{block_size // 16}, 2, {D // 8}, 8, 8] (16-slot tiles)")
-    if block_size % 8 or tuple(v_cache.shape) != (nb, num_kv_heads, block_size // 8, D, 8):
+                                       f"{block_size // 16}, 2, {D // E}, 8, {E}] (16-slot tiles)")
+    if block_size % E or tuple(v_cache.shape) != (nb, num_kv_heads, block_size // E, D, E):
         raise PaError(ERR_INVALID_ARG, f"v_cache must be [num_blocks, {num_kv_heads}, "
-                                       f"{block_size // 8}, {D}, 8]")
+                                       f"{block_size // E}, {D}, {E}]")
     B = block_tables.shape[0]
     if block_tables.dim() != 2 or seq_lens.shape != (B,) or query_lens.shape != (B,):
         raise PaError(ERR_INVALID_ARG, "block_tables [B, M], seq_lens [B], query_lens [B]")
@@ -212,7 +242,7 @@ def _validate(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, num_
 def decode(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, scale, window,
            num_kv_heads, block_size, max_seq_len, max_query_len=None, workspace=None,
            stream=None, path=0, part_size=0, waves=0, event_begin=None, event_end=None,
-           schedule=0, loads=0):
+           schedule=0, loads=0, k_scale=None, v_scale=None):
     """Runs pa_decode_ex on torch tensors; returns ``out``.
 
     ``max_seq_len`` / ``max_query_len`` are host-known upper bounds of the
@@ -226,7 +256,8 @@ def decode(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, scale, 
         max_query_len = int(q.shape[0]) if block_tables.shape[0] else 1
         max_query_len = max(1, min(max_query_len, int(max_seq_len)))
     dims = dims_for(q, k_cache, block_tables, max_query_len, max_seq_len)
-    opts = make_options(path, part_size, waves, event_begin, event_end, schedule, loads)
+    opts = make_options(path, part_size, waves, event_begin, event_end, schedule, loads,
+                        k_scale, v_scale)
     need = workspace_size(dims, window, num_kv_heads, block_size, path=path,
                           part_size=part_size, waves=waves, schedule=schedule)
     if workspace is None and need:
@@ -275,12 +306,13 @@ class Prepared:
     def __init__(self, out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, scale, window,
                  num_kv_heads, block_size, max_seq_len, max_query_len, workspace=None,
                  stream=None, path=0, part_size=0, waves=0, event_begin=None, event_end=None,
-                 schedule=0, loads=0):
+                 schedule=0, loads=0, k_scale=None, v_scale=None):
         import torch
         _validate(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, num_kv_heads,
                   block_size)
         self.dims = dims_for(q, k_cache, block_tables, max_query_len, max_seq_len)
-        self.opts = make_options(path, part_size, waves, event_begin, event_end, schedule, loads)
+        self.opts = make_options(path, part_size, waves, event_begin, event_end, schedule, loads,
+                                 k_scale, v_scale)
         self._events = (event_begin, event_end)
         self.plan = plan(self.dims, window, num_kv_heads, block_size,
                          num_cus=torch.cuda.get_device_properties(q.device).multi_processor_count,
@@ -291,7 +323,7 @@ class Prepared:
         if workspace is None and need:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         self.workspace = workspace
-        self._keep = (out, q, k_cache, v_cache, block_tables, seq_lens, query_lens)
+        self._keep = (out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, k_scale, v_scale)
         vp = ctypes.c_void_p
         self.args = (
             vp(out.data_ptr()), vp(q.data_ptr()), vp(k_cache.data_ptr()), vp(v_cache.data_ptr()),

@@ -75,6 +75,15 @@ __host__ __device__ inline int k_slot_offset(int slot, int D) {
   return (slot >> 4) * (16 * D) + ((u >> 2) & 1) * (8 * D) + ((u & 3) | ((u >> 3) << 2)) * 8;
 }
 
+// The same slab addressed in bytes for 16-byte columns (bf16: 8 dims, FP8:
+// 16 dims per column); row_bytes = D * element size.  Byte offset of
+// (slot, column 0); column c adds 128 * c.
+__host__ __device__ inline int k_slot_bytes(int slot, int row_bytes) {
+  const int u = slot & 15;
+  return (slot >> 4) * (16 * row_bytes) + ((u >> 2) & 1) * (8 * row_bytes) +
+         ((u & 3) | ((u >> 3) << 2)) * 16;
+}
+
 // Exclusive prefix sum of query_lens[0 .. b) computed by one wave; every lane
 // returns the sum.  Gives the first q/out row of sequence b in the packed
 // [sum q_b, H_q, D] layout.
@@ -95,8 +104,8 @@ __device__ inline float bf16_bits_to_f32(uint32_t bits16) {
 struct PartArgs {
   void* out;                   // [T, H_q, D] (one-shot sequences)
   const void* q;               // [T, H_q, D]
-  const void* k_cache;         // [num_blocks, H_kv, bs, D]
-  const void* v_cache;         // [num_blocks, H_kv, bs/8, D, 8]
+  const void* k_cache;         // [num_blocks, H_kv, bs/16, 2, D/E, 8, E] (E = 8; FP8: 16)
+  const void* v_cache;         // [num_blocks, H_kv, bs/E, D, E]
   const int32_t* block_tables; // [B, max_blocks_per_seq]
   const int32_t* seq_lens;     // [B]
   const int32_t* query_lens;   // [B]
@@ -115,6 +124,8 @@ struct PartArgs {
   int log2_bs;
   int max_blocks_per_seq;
   int batch;
+  const float* k_scale;        // FP8 KV: device scalars, K = code * k_scale, V = code * v_scale
+  const float* v_scale;        // (null for native caches)
 };
 
 // Work-item of a partition workgroup.  The grid is 1-D and ordered with the

@@ -62,6 +62,10 @@ pa_status check_shape(const pa_dims* d, int32_t window, int32_t num_kv_heads, in
     return fail(PA_ERR_INVALID_ARG, "batch %d outside [0, 65535]", d->batch);
   if (d->dtype != PA_F32 && d->dtype != PA_BF16)
     return fail(PA_ERR_INVALID_ARG, "dtype %d is neither PA_F32 nor PA_BF16", d->dtype);
+  if (d->kv_format != PA_KV_NATIVE && d->kv_format != PA_KV_FP8_E4M3)
+    return fail(PA_ERR_INVALID_ARG, "kv_format %d unknown", d->kv_format);
+  if (d->kv_format == PA_KV_FP8_E4M3 && d->dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "an FP8 KV cache needs bf16 q and out");
   if (d->head_dim != 64 && d->head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", d->head_dim);
   if (num_kv_heads < 1 || num_kv_heads > 65535)
@@ -103,13 +107,16 @@ pa_status make_plan(const pa_dims* d, int32_t window, int32_t hkv, int32_t bs, i
     return fail(PA_ERR_INVALID_ARG, "path %d unknown", path_req);
   if (path_req == PA_PATH_AUTO) {
     // fp32 inputs never take reduced-precision products.  For bf16 the matrix
-    // cores are the measured choice at every row count (kernels).
+    // cores are faster than the vector kernel at every row count measured on
+    // MI355X (R = 4 included).
     r.path = d->dtype == PA_F32 ? PA_PATH_VALU : PA_PATH_MFMA;
   } else {
     r.path = path_req;
   }
   if (r.path == PA_PATH_MFMA && d->dtype != PA_BF16)
     return fail(PA_ERR_UNSUPPORTED, "the matrix-core path needs bf16 inputs");
+  if (r.path != PA_PATH_MFMA && d->kv_format == PA_KV_FP8_E4M3)
+    return fail(PA_ERR_UNSUPPORTED, "an FP8 KV cache needs the matrix-core path");
   const int nrt = (r.rows + 15) / 16;
   if (r.path == PA_PATH_MFMA) {
     const int w_req = o ? o->waves : 0;
@@ -174,7 +181,7 @@ pa_status make_plan(const pa_dims* d, int32_t window, int32_t hkv, int32_t bs, i
   // MALL, 256 MB) nothing is reused and non-temporal loads stream faster.
   const int loads_req = o ? o->loads : 0;
   if (loads_req < 0 || loads_req > 2) return fail(PA_ERR_INVALID_ARG, "loads %d unknown", loads_req);
-  const int64_t elem = d->dtype == PA_F32 ? 4 : 2;
+  const int64_t elem = d->kv_format == PA_KV_FP8_E4M3 ? 1 : (d->dtype == PA_F32 ? 4 : 2);
   const int64_t kv_positions = std::min<int64_t>((int64_t)d->batch * r.span_max,
                                                  (int64_t)d->num_blocks * bs);
   const bool big = kv_positions * hkv * d->head_dim * 2 * elem > kLastLevelCacheBytes;
@@ -232,37 +239,40 @@ int resident_wgs(const void* fn, int threads, int cus) {
   return cus;
 }
 
-template <int D, int NRT, int NW, bool STREAM>
+template <int D, int NRT, int NW, bool STREAM, bool KV8>
 void launch_mfma_inst(dim3 grid, bool persistent, int cus, hipStream_t s, const pa::PartArgs& a) {
   if (persistent) {
-    const void* fn = (const void*)pa::part_mfma_ps<D, NRT, NW, STREAM>;
+    const void* fn = (const void*)pa::part_mfma_ps<D, NRT, NW, STREAM, KV8>;
     const dim3 pgrid(resident_wgs(fn, 64 * NW, cus));
-    hipLaunchKernelGGL((pa::part_mfma_ps<D, NRT, NW, STREAM>), pgrid, dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((pa::part_mfma_ps<D, NRT, NW, STREAM, KV8>), pgrid, dim3(64 * NW), 0, s, a);
   } else {
-    hipLaunchKernelGGL((pa::part_mfma<D, NRT, NW, STREAM>), grid, dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((pa::part_mfma<D, NRT, NW, STREAM, KV8>), grid, dim3(64 * NW), 0, s, a);
   }
 }
 
-template <int D, bool STREAM>
-bool launch_mfma_loads(int nrt, int nw, dim3 grid, bool persistent, int cus, hipStream_t s,
-                    const pa::PartArgs& a) {
+template <int D, bool STREAM, bool KV8>
+bool launch_mfma_shape(int nrt, int nw, dim3 grid, bool persistent, int cus, hipStream_t s,
+                       const pa::PartArgs& a) {
   switch (nrt * 8 + nw) {
-    case 1 * 8 + 1: launch_mfma_inst<D, 1, 1, STREAM>(grid, persistent, cus, s, a); return true;
-    case 1 * 8 + 2: launch_mfma_inst<D, 1, 2, STREAM>(grid, persistent, cus, s, a); return true;
-    case 1 * 8 + 4: launch_mfma_inst<D, 1, 4, STREAM>(grid, persistent, cus, s, a); return true;
-    case 2 * 8 + 1: launch_mfma_inst<D, 2, 1, STREAM>(grid, persistent, cus, s, a); return true;
-    case 2 * 8 + 2: launch_mfma_inst<D, 2, 2, STREAM>(grid, persistent, cus, s, a); return true;
-    case 3 * 8 + 1: launch_mfma_inst<D, 3, 1, STREAM>(grid, persistent, cus, s, a); return true;
-    case 4 * 8 + 1: launch_mfma_inst<D, 4, 1, STREAM>(grid, persistent, cus, s, a); return true;
+    case 1 * 8 + 1: launch_mfma_inst<D, 1, 1, STREAM, KV8>(grid, persistent, cus, s, a); return true;
+    case 1 * 8 + 2: launch_mfma_inst<D, 1, 2, STREAM, KV8>(grid, persistent, cus, s, a); return true;
+    case 1 * 8 + 4: launch_mfma_inst<D, 1, 4, STREAM, KV8>(grid, persistent, cus, s, a); return true;
+    case 2 * 8 + 1: launch_mfma_inst<D, 2, 1, STREAM, KV8>(grid, persistent, cus, s, a); return true;
+    case 2 * 8 + 2: launch_mfma_inst<D, 2, 2, STREAM, KV8>(grid, persistent, cus, s, a); return true;
+    case 3 * 8 + 1: launch_mfma_inst<D, 3, 1, STREAM, KV8>(grid, persistent, cus, s, a); return true;
+    case 4 * 8 + 1: launch_mfma_inst<D, 4, 1, STREAM, KV8>(grid, persistent, cus, s, a); return true;
     default: return false;
   }
 }
 
 template <int D>
-bool launch_mfma(int nrt, int nw, dim3 grid, bool persistent, bool streaming, int cus,
+bool launch_mfma(int nrt, int nw, dim3 grid, bool persistent, bool streaming, bool kv8, int cus,
                  hipStream_t s, const pa::PartArgs& a) {
-  return streaming ? launch_mfma_loads<D, true>(nrt, nw, grid, persistent, cus, s, a)
-                   : launch_mfma_loads<D, false>(nrt, nw, grid, persistent, cus, s, a);
+  if (kv8)
+    return streaming ? launch_mfma_shape<D, true, true>(nrt, nw, grid, persistent, cus, s, a)
+                     : launch_mfma_shape<D, false, true>(nrt, nw, grid, persistent, cus, s, a);
+  return streaming ? launch_mfma_shape<D, true, false>(nrt, nw, grid, persistent, cus, s, a)
+                   : launch_mfma_shape<D, false, false>(nrt, nw, grid, persistent, cus, s, a);
 }
 
 pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -280,6 +290,16 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
     return fail(PA_ERR_INVALID_ARG, "int32 arrays must be 4-byte aligned");
   if (workspace && !aligned(workspace, 16))
     return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const bool kv8 = d->kv_format == PA_KV_FP8_E4M3;
+  if (kv8) {
+    // aiter PR #2914 review: FP8 caches without their scales must be refused,
+    // not decoded with a default
+    if (!o || !o->k_scale || !o->v_scale)
+      return fail(PA_ERR_INVALID_ARG,
+                  "an FP8 KV cache needs k_scale and v_scale (pa_decode_ex, pa_options)");
+    if (!aligned(o->k_scale, 4) || !aligned(o->v_scale, 4))
+      return fail(PA_ERR_INVALID_ARG, "k_scale and v_scale must be 4-byte aligned");
+  }
   if (d->batch == 0) return PA_OK;
   int cus = 0;
   st = device_cu_count(&cus);
@@ -292,9 +312,9 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
                 (unsigned long long)p.workspace_bytes);
   if (log_enabled())
     std::fprintf(stderr,
-                 "[pa_decode] B=%d Hq=%d Hkv=%d D=%d bs=%d w=%d R=%d span_max=%d path=%s P=%d NP=%d "
+                 "[pa_decode] B=%d Hq=%d Hkv=%d D=%d bs=%d w=%d kv8=%d R=%d span_max=%d path=%s P=%d NP=%d "
                  "waves=%d one_shot=%d persistent=%d streaming=%d ws=%llu cus=%d\n",
-                 d->batch, d->num_q_heads, hkv, d->head_dim, bs, window, p.rows, p.span_max,
+                 d->batch, d->num_q_heads, hkv, d->head_dim, bs, window, (int)kv8, p.rows, p.span_max,
                  p.path == PA_PATH_MFMA ? "mfma" : "valu", p.part_size, p.num_parts, p.waves,
                  p.one_shot, p.persistent, p.streaming, (unsigned long long)p.workspace_bytes, cus);
 
@@ -325,6 +345,8 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
   a.log2_bs = ilog2_exact(bs);
   a.max_blocks_per_seq = d->max_blocks_per_seq;
   a.batch = d->batch;
+  a.k_scale = kv8 ? o->k_scale : nullptr;
+  a.v_scale = kv8 ? o->v_scale : nullptr;
 
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
@@ -339,8 +361,8 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
   bool ok = true;
   if (p.path == PA_PATH_MFMA) {
     ok = d->head_dim == 64
-             ? launch_mfma<64>(nrt, p.waves, grid, p.persistent, p.streaming, cus, s, a)
-             : launch_mfma<128>(nrt, p.waves, grid, p.persistent, p.streaming, cus, s, a);
+             ? launch_mfma<64>(nrt, p.waves, grid, p.persistent, p.streaming, kv8, cus, s, a)
+             : launch_mfma<128>(nrt, p.waves, grid, p.persistent, p.streaming, kv8, cus, s, a);
   } else if (d->dtype == PA_F32) {
     if (d->head_dim == 64) hipLaunchKernelGGL((pa::part_valu<float, 64>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((pa::part_valu<float, 128>), grid, dim3(256), 0, s, a);

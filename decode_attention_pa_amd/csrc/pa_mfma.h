@@ -42,9 +42,26 @@ __device__ inline bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, 
 // block-table gather; below that size the cached form keeps the KV resident
 // in the 256 MB MALL for the next call.
 template <bool STREAM>
-__device__ inline u32x4 ld_kv(const uint16_t* p) {
+__device__ inline u32x4 ld_kv(const uint8_t* p) {
   if constexpr (STREAM) return __builtin_nontemporal_load((const u32x4*)p);
   else return *(const u32x4*)p;
+}
+// 8-byte form (8 FP8 values of V).
+template <bool STREAM>
+__device__ inline u32x2 ld_kv8(const uint8_t* p) {
+  if constexpr (STREAM) return __builtin_nontemporal_load((const u32x2*)p);
+  else return *(const u32x2*)p;
+}
+
+// Eight OCP E4M3 codes (bytes of a, then of b, in memory order) as bf16.
+// Exact: every E4M3 value is a bf16 value; the unit scale leaves it as is.
+__device__ inline bf16x8 e4m3x8_to_bf16(uint32_t a, uint32_t b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(a, 1.f, false);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(a, 1.f, true);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b, 1.f, false);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b, 1.f, true);
+  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
 // Physical blocks touched by one chunk: the chunk's in-partition positions
@@ -70,12 +87,21 @@ struct ChunkBlocks {
 // With `write_out` (the run is the whole unit) it writes `out`; otherwise its
 // state (max, exp-sum, normalised output) goes to workspace slot `slot` of
 // the unit.  All waves of the workgroup call this with the same arguments.
-template <int D, int NRT, int NW, bool STREAM>
+// KV8: K and V hold OCP E4M3 codes (16 per 16-byte column / V row) that are
+// converted to bf16 in registers; the K scale folds into the logit scale and
+// the V scale into the output normalisation.  With 16 dims per K column, one
+// 16-byte load feeds two k-steps: k-step 2c + x of lane group lg takes dims
+// 16 * (4c + lg) + 8x .. +7, and Q^T is loaded in the same order (a
+// contraction may visit its index in any order, as long as both operands
+// agree).
+template <int D, int NRT, int NW, bool STREAM, bool KV8>
 __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L, int q, int qoff,
                                          const SeqView& sv, int j_first, int j_last, int slot,
                                          bool write_out) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
+  constexpr int ES = KV8 ? 1 : 2;        // bytes per cached element
+  constexpr int KL = KV8 ? KS / 2 : KS;  // 16-byte K loads per tile
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ln = lane & 15, lg = lane >> 4;
@@ -89,9 +115,9 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
   const int bs_mask = (1 << log2_bs) - 1;
 
   const int32_t* __restrict__ table = a.block_tables + (size_t)b * a.max_blocks_per_seq;
-  const uint16_t* __restrict__ kc = (const uint16_t*)a.k_cache;
-  const uint16_t* __restrict__ vc = (const uint16_t*)a.v_cache;
-  const size_t slab = (size_t)D << log2_bs;                 // elements per (block, head)
+  const uint8_t* __restrict__ kc = (const uint8_t*)a.k_cache;
+  const uint8_t* __restrict__ vc = (const uint8_t*)a.v_cache;
+  const size_t slab = ((size_t)D * ES) << log2_bs;          // bytes per (block, head)
   const size_t blk_stride = slab * (size_t)a.num_kv_heads;
   const size_t head_off = slab * (size_t)h;
 
@@ -113,7 +139,10 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
       const uint16_t* qp =
           (const uint16_t*)a.q + ((size_t)(qoff + i) * a.num_q_heads + (size_t)h * G + g) * D;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) qf[rt][s] = as_bf16x8(*(const u32x4*)(qp + (4 * s + lg) * 8));
+      for (int s = 0; s < KS; ++s) {
+        const int d0 = KV8 ? 16 * (4 * (s >> 1) + lg) + 8 * (s & 1) : 8 * (4 * s + lg);
+        qf[rt][s] = as_bf16x8(*(const u32x4*)(qp + d0));
+      }
     } else {
       tlo[rt] = 0x7fffffff;
       thi[rt] = -1;
@@ -134,35 +163,57 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
     return cb;
   };
   // K rows: lane (ln, lg) of tile t holds position 8*(ln/4) + 4*t + ln%4 of
-  // the chunk, dims 8*lg + 32*s .. +7 for k-step s.  In the tiled K layout
-  // these are place ln%8 of half t of 16-slot group ln/8, column 4*s + lg:
-  // each load instruction reads two runs of 512 contiguous bytes.
-  auto load_k = [&](int k, const ChunkBlocks& cb, u32x4 (&kr)[2][KS]) {
+  // the chunk and, per load, the 16-byte column 4*c + lg of it (bf16: the
+  // dims of k-step c; FP8: those of k-steps 2c and 2c+1).  In the tiled K
+  // layout that is place ln%8 of half t of 16-slot group ln/8: each load
+  // instruction reads two runs of 512 contiguous bytes.
+  auto load_k = [&](int k, const ChunkBlocks& cb, u32x4 (&kr)[2][KL]) {
     const int cs = cb0 + k * kChunk;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       int pos = cs + 8 * (ln >> 2) + 4 * t + (ln & 3);
       pos = min(max(pos, ps), pe - 1);  // clamp: never touch blocks outside the span
       const int blk = (pos >> log2_bs) == cb.first_idx ? cb.first : cb.second;
-      const uint16_t* kp = kc + (size_t)blk * blk_stride + head_off +
-                           k_slot_offset(pos & bs_mask, D) + lg * 64;
+      const uint8_t* kp = kc + (size_t)blk * blk_stride + head_off +
+                          k_slot_bytes(pos & bs_mask, D * ES) + lg * 128;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) kr[t][s] = ld_kv<STREAM>(kp + s * 256);
+      for (int c = 0; c < KL; ++c) kr[t][c] = ld_kv<STREAM>(kp + c * 512);
     }
   };
   // V^T columns: lane (ln, lg) holds dim 16*dt + ln, positions 8*lg .. +7.
+  // bf16: 8-slot group = a [D][8] tile, one 16-byte load; the 16 lanes of a
+  // lane group read 256 contiguous bytes.  FP8: 16-slot group = a [D][16]
+  // tile, the 8 bytes of half lg % 2 of the dim's row; lane groups 2j and
+  // 2j+1 together read 256 contiguous bytes.
   auto load_v = [&](int k, const ChunkBlocks& cb, u32x4 (&vr)[DT]) {
     const int cs = cb0 + k * kChunk;
     int p8 = cs + 8 * lg;
     if (p8 + 8 <= ps || p8 >= pe) p8 = max(cs, ps) & ~7;  // wholly outside: any valid group, zeroed later
     else p8 = max(p8, ps & ~7);
     const int blk = (p8 >> log2_bs) == cb.first_idx ? cb.first : cb.second;
-    // 8-slot group (p8 & bs_mask) / 8 of the block is a [D][8] tile: the 16
-    // lanes of a lane group read 16 consecutive dims = 256 contiguous bytes
-    const uint16_t* vp = vc + (size_t)blk * blk_stride + head_off +
-                         (size_t)((p8 & bs_mask) >> 3) * (D * 8) + ln * 8;
+    if constexpr (KV8) {
+      const uint8_t* vp = vc + (size_t)blk * blk_stride + head_off +
+                          (size_t)((p8 & bs_mask) >> 4) * (D * 16) + ln * 16 + (p8 & 8);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) vr[dt] = ld_kv<STREAM>(vp + 16 * 8 * dt);
+      for (int dt = 0; dt < DT; ++dt) {
+        const u32x2 w = ld_kv8<STREAM>(vp + 256 * dt);
+        vr[dt] = u32x4{w[0], w[1], 0u, 0u};
+      }
+    } else {
+      const uint8_t* vp = vc + (size_t)blk * blk_stride + head_off +
+                          (size_t)((p8 & bs_mask) >> 3) * (D * 16) + ln * 16;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) vr[dt] = ld_kv<STREAM>(vp + 256 * dt);
+    }
+  };
+  // bf16 A operand of k-step s of tile t
+  auto k_operand = [&](const u32x4 (&kr)[2][KL], int t, int s) -> bf16x8 {
+    if constexpr (KV8) {
+      const u32x4& w = kr[t][s >> 1];
+      return (s & 1) ? e4m3x8_to_bf16(w[2], w[3]) : e4m3x8_to_bf16(w[0], w[1]);
+    } else {
+      return as_bf16x8(kr[t][s]);
+    }
   };
 
   f32x4 o[NRT][DT];
@@ -174,7 +225,12 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const float scale_log2 = a.scale_log2;
+  float scale_log2 = a.scale_log2;
+  float v_scale = 1.f;
+  if constexpr (KV8) {
+    scale_log2 *= *a.k_scale;
+    v_scale = *a.v_scale;
+  }
 
   // Software pipeline, one chunk deep: the next chunk's K rows are requested
   // as soon as QK has consumed the current ones, its V columns as soon as PV
@@ -182,7 +238,7 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
   // issued unconditionally (the last iteration re-requests its own chunk, a
   // cache hit) so that the wait counts are the same on every path.
   int k = wave;
-  u32x4 kr[2][KS], vr[DT];
+  u32x4 kr[2][KL], vr[DT];
   ChunkBlocks nb = {0, 0, 0};
   if (k < nck) {
     const ChunkBlocks cb = blocks_of(k);
@@ -200,8 +256,8 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
       f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[0][s]), qf[rt][s], sa, 0, 0, 0);
-        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[1][s]), qf[rt][s], sb, 0, 0, 0);
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(kr, 0, s), qf[rt][s], sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(kr, 1, s), qf[rt][s], sb, 0, 0, 0);
       }
       // visible iff tlo <= t <= thi, as one unsigned comparison (rows that
       // see nothing have tlo = 2^31 - 1, thi = -1: no t >= 0 passes)
@@ -247,6 +303,11 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
     // loads to arrive, and waiting for them earlier would serialise the
     // next chunk's K requests behind them.
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (KV8) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        vr[dt] = __builtin_bit_cast(u32x4, e4m3x8_to_bf16(vr[dt][0], vr[dt][1]));
+    }
     if (cs < ps || cs + kChunk > pe) {
       // Edge chunk: zero V entries of positions outside [ps, pe) so that a
       // zero weight never meets a stale, possibly NaN, value.
@@ -330,7 +391,7 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
     for (int rt = 0; rt < NRT; ++rt) {
       const int n = rt * 16 + ln;
       if (n >= rows_b) continue;
-      const float inv = lrun[rt] > 0.f ? 1.f / lrun[rt] : 0.f;
+      const float inv = lrun[rt] > 0.f ? v_scale / lrun[rt] : 0.f;
       if (one_shot) {
         const int i = n / G;
         const int g = n - i * G;
@@ -358,7 +419,7 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
 }
 
 // Grid schedule: one workgroup per (partition, sequence, KV head).
-template <int D, int NRT, int NW, bool STREAM>
+template <int D, int NRT, int NW, bool STREAM, bool KV8>
 __global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
   const PartItem it = part_item(a);
   const int L = a.seq_lens[it.b];
@@ -366,7 +427,7 @@ __global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
   const SeqView sv = seq_view(L, q, a.window, a.part_size);
   if (it.j >= sv.nparts) return;  // empty partition: contributes nothing
   const int qoff = wave_row_offset(a.query_lens, it.b);
-  mfma_run<D, NRT, NW, STREAM>(a, it.b, it.h, L, q, qoff, sv, it.j, it.j, it.j, sv.nparts == 1);
+  mfma_run<D, NRT, NW, STREAM, KV8>(a, it.b, it.h, L, q, qoff, sv, it.j, it.j, it.j, sv.nparts == 1);
 }
 
 // Persistent schedule (aiter PR #2914: "PS" decode): a grid of about one
@@ -379,7 +440,7 @@ __global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
 // whole unit writes `out`; otherwise it stores its state in slot k = its
 // ordinal among the unit's runs, and the unit's last run records the number
 // of states for the merge (0 when the unit was written directly).
-template <int D, int NRT, int NW, bool STREAM>
+template <int D, int NRT, int NW, bool STREAM, bool KV8>
 __global__ __launch_bounds__(64 * NW) void part_mfma_ps(PartArgs a) {
   constexpr int NT = 64 * NW;
   __shared__ int s_np[kPsMaxBatch + 1];  // exclusive prefix of partitions per sequence
@@ -460,7 +521,7 @@ __global__ __launch_bounds__(64 * NW) void part_mfma_ps(PartArgs a) {
     const long w_first = ((A + 1) * W + total - 1) / total - 1;
     const int slot = (int)((long)blockIdx.x - w_first);
     const bool whole = (j1 == 0 && j2 == np_b - 1);
-    mfma_run<D, NRT, NW, STREAM>(a, b, h, L, q, s_q[b], sv, j1, j2, slot, whole);
+    mfma_run<D, NRT, NW, STREAM, KV8>(a, b, h, L, q, s_q[b], sv, j1, j2, slot, whole);
     // (one-shot plans have no workspace: every unit is whole and no merge runs)
     if (j2 == np_b - 1 && tid == 0 && a.ws_runs != nullptr)
       a.ws_runs[(size_t)b * H + h] = whole ? 0 : slot + 1;

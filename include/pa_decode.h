@@ -28,22 +28,24 @@
  * Memory layouts (row-major, contiguous, all device memory):
  *   q, out        [T, H_q, D], T = sum_b q_b; sequence b owns rows
  *                 qoff_b .. qoff_b + q_b - 1, qoff_b = q_0 + ... + q_{b-1}
- *   k_cache       [num_blocks, H_kv, block_size/16, 2, D/8, 8, 8]: slots grouped
- *                 by 16; slot s of a group lives in half (s >> 2) & 1 at place
+ *   k_cache       [num_blocks, H_kv, block_size/16, 2, D/E, 8, E] with E = 8 for
+ *                 bf16 and fp32 and E = 16 for FP8: slots grouped by 16; slot s
+ *                 of a group lives in half (s >> 2) & 1 at place
  *                 (s & 3) | ((s >> 3) << 2), i.e. half 0 holds slots 0-3 and
- *                 8-11, half 1 slots 4-7 and 12-15; each half is a [D/8][8][8]
- *                 tile (8-dim column, place, dim within the column), so 16
- *                 contiguous bytes hold 8 dims of one slot and a column of a
- *                 half is 128 contiguous bytes
+ *                 8-11, half 1 slots 4-7 and 12-15; each half is a [D/E][8][E]
+ *                 tile (column of E dims, place, dim within the column).  For
+ *                 bf16 and FP8 a column of one slot is 16 contiguous bytes and a
+ *                 column of a half 128
  *   v_cache       [num_blocks, H_kv, block_size/8, D, 8]: slots grouped by 8;
  *                 slot s of a block lives at [s/8][d][s%8] (a [D, 8] tile per
  *                 group: 16 contiguous bytes hold one dim of 8 consecutive
- *                 positions)
+ *                 positions).  FP8: groups of 16, [block_size/16][D][16]
  *   block_tables  int32 [B, max_blocks_per_seq]; position t of sequence b
  *                 lives in physical block block_tables[b][t / block_size] at
  *                 slot t % block_size
  *   seq_lens, query_lens   int32 [B]
- * q, k_cache, v_cache and out share one element type (pa_dims.dtype).
+ * q and out share one element type (pa_dims.dtype); k_cache and v_cache share
+ * it too, or hold FP8 codes (pa_dims.kv_format).
  *
  * Device-side preconditions (not checked on the hot path; violating them is
  * undefined behaviour):  0 <= q_b <= L_b <= max_seq_len, q_b <= max_query_len,
@@ -85,6 +87,17 @@ typedef enum pa_dtype {
   PA_BF16 = 1               /* bfloat16 */
 } pa_dtype;
 
+/* Element format of k_cache and v_cache. */
+typedef enum pa_kv_format {
+  PA_KV_NATIVE = 0,         /* K and V in pa_dims.dtype */
+  PA_KV_FP8_E4M3 = 1        /* OCP E4M3 codes (one byte) with per-tensor scales: value =
+                               code * (*k_scale) for K, code * (*v_scale) for V.  bf16
+                               q/out and the matrix-core path only.  aiter PR #2914
+                               (review of pa_decode_gluon): an FP8 cache must come with
+                               its key / value scales, and calls without them are
+                               rejected (PA_ERR_INVALID_ARG) */
+} pa_kv_format;
+
 /* Shapes a raw-pointer interface cannot infer.  All host-side values. */
 typedef struct pa_dims {
   int32_t batch;              /* B >= 0 */
@@ -94,7 +107,8 @@ typedef struct pa_dims {
   int32_t max_seq_len;        /* upper bound on seq_lens[b], >= 1 */
   int32_t max_blocks_per_seq; /* row stride of block_tables, >= ceil(max_seq_len/block_size) */
   int32_t num_blocks;         /* physical blocks in each cache, >= 1 */
-  int32_t dtype;              /* pa_dtype of q, k_cache, v_cache and out */
+  int32_t dtype;              /* pa_dtype of q and out (and of k_cache, v_cache when native) */
+  int32_t kv_format;          /* pa_kv_format of k_cache and v_cache */
 } pa_dims;
 
 /* Kernel families for the partition step. */
@@ -135,6 +149,9 @@ typedef struct pa_options {
   void* event_begin;          /* hipEvent_t recorded on the stream just before the
                                  partition kernel, or NULL */
   void* event_end;            /* hipEvent_t recorded just after it, or NULL */
+  const float* k_scale;       /* PA_KV_FP8_E4M3: device pointer to the K scale (one float,
+                                 4-byte aligned); required then, ignored otherwise */
+  const float* v_scale;       /* PA_KV_FP8_E4M3: device pointer to the V scale */
 } pa_options;
 
 /*

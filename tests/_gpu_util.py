@@ -21,9 +21,13 @@ def say(*a):
 
 
 def run_gpu(case, out=None, **opts):
-    """One pa_decode call on the case's tensors; returns the output tensor."""
+    """One pa_decode call on the case's tensors; returns the output tensor.
+    FP8 cases pass their scales unless the caller overrides them."""
     if out is None:
         out = case.new_out().fill_(float("nan"))
+    if case.k_scale is not None:
+        opts.setdefault("k_scale", case.k_scale)
+        opts.setdefault("v_scale", case.v_scale)
     pa.decode(out, case.q, case.k_cache, case.v_cache, case.block_tables, case.seq_lens,
               case.query_lens, case.scale, case.window, case.w.num_kv_heads, case.w.block_size,
               max_seq_len=case.w.max_seq_len, max_query_len=max(case.w.query_len,
@@ -48,9 +52,9 @@ def oracle_inputs(case, seqs=None):
     need = sorted(set(int(x) for b in seqs for x in sp[b]["blocks"] if x >= 0))
     remap = {p: i + 1 for i, p in enumerate(need)}
     ids = torch.tensor(need, dtype=torch.long, device=case.k_cache.device)
-    k = case.k_cache.index_select(0, ids).float().cpu().numpy() if need else \
+    k = _host_values(case.k_cache.index_select(0, ids), case.w.k_scale) if need else \
         np.zeros((0,) + tuple(case.k_cache.shape[1:]), np.float32)
-    v = case.v_cache.index_select(0, ids).float().cpu().numpy() if need else \
+    v = _host_values(case.v_cache.index_select(0, ids), case.w.v_scale) if need else \
         np.zeros((0,) + tuple(case.v_cache.shape[1:]), np.float32)
     k = np.concatenate([np.full((1,) + k.shape[1:], np.nan, np.float32), k])
     v = np.concatenate([np.full((1,) + v.shape[1:], np.nan, np.float32), v])
@@ -66,6 +70,13 @@ def oracle_inputs(case, seqs=None):
                 query_lens=np.array([case.query_lens_host[b] for b in seqs]),
                 scale=case.scale, window=case.window, num_kv_heads=case.w.num_kv_heads,
                 block_size=case.w.block_size), rows
+
+
+def _host_values(t, scale):
+    """Cache blocks as host values: FP8 codes dequantized by the oracle."""
+    if t.dtype == torch.float8_e4m3fn:
+        return ref.dequantize(t.view(torch.uint8).cpu().numpy(), scale)
+    return t.float().cpu().numpy()
 
 
 def oracle_out(case, seqs=None):

@@ -53,7 +53,8 @@ def dims_of(w: workloads.Workload, max_query_len=None, **over):
     d = dict(batch=w.batch, num_q_heads=w.num_q_heads, head_dim=w.head_dim,
              max_query_len=w.query_len if max_query_len is None else max_query_len, max_seq_len=w.max_seq_len,
              max_blocks_per_seq=w.max_blocks_per_seq, num_blocks=1000,
-             dtype=pa.F32 if w.dtype == "f32" else pa.BF16)
+             dtype=pa.F32 if w.dtype == "f32" else pa.BF16,
+             kv_format=pa.KV_FP8_E4M3 if w.kv_dtype == "fp8" else pa.KV_NATIVE)
     d.update(over)
     return pa.make_dims(**d)
 
@@ -217,6 +218,37 @@ def test_decode_validates_before_touching_a_device(lib):
     assert st == pa.ERR_INVALID_ARG
     st = lib.pa_decode(*args[:7], ctypes.c_float(0.1), 0, 8, 16, None, None, 0, None)
     assert st == pa.ERR_INVALID_ARG
+    # an FP8 cache without its scales is refused (pa_decode has no way to pass
+    # them; pa_decode_ex needs both, 4-byte aligned)
+    d8 = dims_of(w, kv_format=pa.KV_FP8_E4M3)
+    st = lib.pa_decode(*args[:7], ctypes.c_float(0.1), 0, 8, 16, ctypes.byref(d8), None, 0, None)
+    assert st == pa.ERR_INVALID_ARG and b"k_scale" in lib.pa_last_error()
+    for ks, vs in ((None, None), (P(4096), None), (None, P(4096)), (P(4098), P(4096))):
+        o = pa.make_options()
+        o.k_scale, o.v_scale = ks, vs
+        st = lib.pa_decode_ex(*args[:7], ctypes.c_float(0.1), 0, 8, 16, ctypes.byref(d8), None, 0,
+                              None, ctypes.byref(o))
+        assert st == pa.ERR_INVALID_ARG, (ks, vs)
+
+
+def test_fp8_kv_format_rules(lib):
+    w = workloads.WORKLOADS["gqa_fp8kv"]
+    p = pa.plan(dims_of(w, kv_format=pa.KV_FP8_E4M3), 0, 8, 16)
+    assert p["path"] == pa.PATH_MFMA
+    for over, kw, code in [(dict(kv_format=2), {}, pa.ERR_INVALID_ARG),
+                           (dict(kv_format=pa.KV_FP8_E4M3, dtype=pa.F32), {}, pa.ERR_UNSUPPORTED),
+                           (dict(kv_format=pa.KV_FP8_E4M3), dict(path=pa.PATH_VALU),
+                            pa.ERR_UNSUPPORTED)]:
+        with pytest.raises(pa.PaError) as e:
+            pa.plan(dims_of(w, **over), 0, 8, 16, **kw)
+        assert e.value.status == code, over
+    # the load form follows the KV bytes: one byte per element halves them
+    big = dims_of(w, num_blocks=10899, kv_format=pa.KV_FP8_E4M3)      # 341 MiB of FP8
+    assert pa.plan(big, 0, 8, 16)["streaming"] == 1
+    half = dims_of(w, num_blocks=6000, kv_format=pa.KV_FP8_E4M3)      # 188 MiB of FP8
+    assert pa.plan(half, 0, 8, 16)["streaming"] == 0
+    native = dims_of(w, num_blocks=6000, kv_format=pa.KV_NATIVE)        # 375 MiB of bf16
+    assert pa.plan(native, 0, 8, 16)["streaming"] == 1
 
 
 def test_empty_batch_is_a_no_op(lib):
