@@ -141,7 +141,7 @@ def cpu_baseline(case, out_gpu, budget_s: float, per_call_bytes: int) -> dict:
     order = list(range(w.batch))
     done, t_total, bytes_done = [], 0.0, 0
     max_err = 0.0
-    s = 2 if w.dtype == "bf16" else 4
+    s = 1 if w.kv_dtype == "fp8" else (2 if w.dtype == "bf16" else 4)   # bytes per K / V element
     with threadpool_limits(limits=1):
         for b in order:
             inp, rows = oracle_inputs(case, [b])

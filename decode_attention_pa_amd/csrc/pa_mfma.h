@@ -167,17 +167,20 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
   // dims of k-step c; FP8: those of k-steps 2c and 2c+1).  In the tiled K
   // layout that is place ln%8 of half t of 16-slot group ln/8: each load
   // instruction reads two runs of 512 contiguous bytes.
-  auto load_k = [&](int k, const ChunkBlocks& cb, u32x4 (&kr)[2][KL]) {
+  // `dummy` (wave-uniform): the loads only keep the wait counts static past
+  // the last chunk; every lane then reads the same 16 bytes, so they cost one
+  // line instead of the chunk (non-temporal loads would fetch it again).
+  auto load_k = [&](int k, const ChunkBlocks& cb, u32x4 (&kr)[2][KL], bool dummy) {
     const int cs = cb0 + k * kChunk;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       int pos = cs + 8 * (ln >> 2) + 4 * t + (ln & 3);
       pos = min(max(pos, ps), pe - 1);  // clamp: never touch blocks outside the span
       const int blk = (pos >> log2_bs) == cb.first_idx ? cb.first : cb.second;
-      const uint8_t* kp = kc + (size_t)blk * blk_stride + head_off +
-                          k_slot_bytes(pos & bs_mask, D * ES) + lg * 128;
+      const int in_slab = dummy ? 0 : k_slot_bytes(pos & bs_mask, D * ES) + lg * 128;
+      const uint8_t* kp = kc + (size_t)(dummy ? cb.first : blk) * blk_stride + head_off + in_slab;
 #pragma unroll
-      for (int c = 0; c < KL; ++c) kr[t][c] = ld_kv<STREAM>(kp + c * 512);
+      for (int c = 0; c < KL; ++c) kr[t][c] = ld_kv<STREAM>(kp + (dummy ? 0 : c * 512));
     }
   };
   // V^T columns: lane (ln, lg) holds dim 16*dt + ln, positions 8*lg .. +7.
@@ -185,25 +188,24 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
   // lane group read 256 contiguous bytes.  FP8: 16-slot group = a [D][16]
   // tile, the 8 bytes of half lg % 2 of the dim's row; lane groups 2j and
   // 2j+1 together read 256 contiguous bytes.
-  auto load_v = [&](int k, const ChunkBlocks& cb, u32x4 (&vr)[DT]) {
+  auto load_v = [&](int k, const ChunkBlocks& cb, u32x4 (&vr)[DT], bool dummy) {
     const int cs = cb0 + k * kChunk;
     int p8 = cs + 8 * lg;
     if (p8 + 8 <= ps || p8 >= pe) p8 = max(cs, ps) & ~7;  // wholly outside: any valid group, zeroed later
     else p8 = max(p8, ps & ~7);
-    const int blk = (p8 >> log2_bs) == cb.first_idx ? cb.first : cb.second;
+    const int blk = dummy ? cb.first : ((p8 >> log2_bs) == cb.first_idx ? cb.first : cb.second);
+    const uint8_t* vb = vc + (size_t)blk * blk_stride + head_off;
     if constexpr (KV8) {
-      const uint8_t* vp = vc + (size_t)blk * blk_stride + head_off +
-                          (size_t)((p8 & bs_mask) >> 4) * (D * 16) + ln * 16 + (p8 & 8);
+      const uint8_t* vp = vb + (dummy ? 0 : ((p8 & bs_mask) >> 4) * (D * 16) + ln * 16 + (p8 & 8));
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const u32x2 w = ld_kv8<STREAM>(vp + 256 * dt);
+        const u32x2 w = ld_kv8<STREAM>(vp + (dummy ? 0 : 256 * dt));
         vr[dt] = u32x4{w[0], w[1], 0u, 0u};
       }
     } else {
-      const uint8_t* vp = vc + (size_t)blk * blk_stride + head_off +
-                          (size_t)((p8 & bs_mask) >> 3) * (D * 16) + ln * 16;
+      const uint8_t* vp = vb + (dummy ? 0 : ((p8 & bs_mask) >> 3) * (D * 16) + ln * 16);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) vr[dt] = ld_kv<STREAM>(vp + 256 * dt);
+      for (int dt = 0; dt < DT; ++dt) vr[dt] = ld_kv<STREAM>(vp + (dummy ? 0 : 256 * dt));
     }
   };
   // bf16 A operand of k-step s of tile t
@@ -235,18 +237,19 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
   // Software pipeline, one chunk deep: the next chunk's K rows are requested
   // as soon as QK has consumed the current ones, its V columns as soon as PV
   // has; block ids run two chunks ahead through the scalar cache.  Loads are
-  // issued unconditionally (the last iteration re-requests its own chunk, a
-  // cache hit) so that the wait counts are the same on every path.
+  // issued unconditionally (after its last chunk a wave issues one-line dummy
+  // loads) so that the wait counts are the same on every path.
   int k = wave;
   u32x4 kr[2][KL], vr[DT];
   ChunkBlocks nb = {0, 0, 0};
   if (k < nck) {
     const ChunkBlocks cb = blocks_of(k);
-    load_k(k, cb, kr);
-    load_v(k, cb, vr);
+    load_k(k, cb, kr, false);
+    load_v(k, cb, vr, false);
     nb = blocks_of(min(k + NW, nck - 1));
   }
   for (; k < nck; k += NW) {
+    const bool past = k + NW >= nck;  // no next chunk for this wave
     const int kn = min(k + NW, nck - 1);
     const int cs = cb0 + k * kChunk;
     const int p8 = cs + 8 * lg;
@@ -297,7 +300,7 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
       }
       lrun[rt] += psum;
     }
-    load_k(kn, nb, kr);
+    load_k(kn, nb, kr, past);
     const ChunkBlocks nb2 = blocks_of(min(k + 2 * NW, nck - 1));
     // Keep V-dependent work below this point: the V columns are the last
     // loads to arrive, and waiting for them earlier would serialise the
@@ -331,7 +334,7 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
     // Request the next V columns only after PV has read these registers
     // (no second register copy of the chunk).
     __builtin_amdgcn_sched_barrier(0);
-    load_v(kn, nb, vr);
+    load_v(kn, nb, vr, past);
     nb = nb2;
   }
 
