@@ -58,6 +58,7 @@ class Plan(ctypes.Structure):
                 ("span_max", ctypes.c_int32), ("part_size", ctypes.c_int32),
                 ("num_parts", ctypes.c_int32), ("waves", ctypes.c_int32),
                 ("one_shot", ctypes.c_int32), ("persistent", ctypes.c_int32),
+                ("row_tiles", ctypes.c_int32), ("row_blocks", ctypes.c_int32),
                 ("streaming", ctypes.c_int32), ("workspace_bytes", ctypes.c_uint64)]
 
     def as_dict(self) -> dict:
@@ -227,8 +228,12 @@ def _validate(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, num_
     T, Hq, D = q.shape
     nb = k_cache.shape[0]
     E = 16 if fp8 else 8                     # elements per 16-byte column / V group
-    if block_size % 16 or D % E or tuple(k_cache.shape) != (nb, num_kv_heads, block_size // 16, 2,
-                                                             D // E, 8, E):
+    if D % E:                                # head dims off the column grid: a row per slot
+        if tuple(k_cache.shape) != (nb, num_kv_heads, block_size, D):
+            raise PaError(ERR_INVALID_ARG, f"k_cache must be [num_blocks, {num_kv_heads}, "
+                                           f"{block_size}, {D}] (head dim not a multiple of {E})")
+    elif block_size % 16 or tuple(k_cache.shape) != (nb, num_kv_heads, block_size // 16, 2,
+                                                     D // E, 8, E):
         raise PaError(ERR_INVALID_ARG, f"k_cache must be [num_blocks, {num_kv_heads}, "
                                        f"{block_size // 16}, 2, {D // E}, 8, {E}] (16-slot tiles)")
     if block_size % E or tuple(v_cache.shape) != (nb, num_kv_heads, block_size // E, D, E):

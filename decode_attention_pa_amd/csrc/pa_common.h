@@ -124,25 +124,33 @@ struct PartArgs {
   int log2_bs;
   int max_blocks_per_seq;
   int batch;
+  int row_blocks;              // workgroups per (partition, sequence, KV head), each taking
+                               // the next rows_per_block packed rows
+  int head_dim;                // D (the vector kernel reads it at run time)
   const float* k_scale;        // FP8 KV: device scalars, K = code * k_scale, V = code * v_scale
   const float* v_scale;        // (null for native caches)
 };
 
 // Work-item of a partition workgroup.  The grid is 1-D and ordered with the
-// KV head fastest and the partition slowest: workgroups are handed to the 8
+// row block, then the KV head fastest and the partition slowest: workgroups
+// are handed to the 8
 // XCDs round-robin by id, so consecutive ids must carry comparable work.
 // (With the partition fastest and 8 partitions per sequence, partition j
 // would always land on XCD j, and high partitions exist only for long
 // sequences.)
 struct PartItem {
-  int j, h, b;
+  int j, h, b, rb;
 };
 
+// Row blocks of one (partition, sequence, KV head) are the fastest index:
+// they read the same K/V, so they run side by side and share its lines.
 __device__ inline PartItem part_item(const PartArgs& a) {
   const int id = blockIdx.x;
   PartItem it;
-  it.h = id % a.num_kv_heads;
-  const int r = id / a.num_kv_heads;
+  it.rb = id % a.row_blocks;
+  const int u = id / a.row_blocks;
+  it.h = u % a.num_kv_heads;
+  const int r = u / a.num_kv_heads;
   it.b = r % a.batch;
   it.j = r / a.batch;
   return it;
@@ -163,6 +171,7 @@ struct ReduceArgs {
   int rows;
   int num_parts;
   int part_size;
+  int head_dim;
 };
 
 }  // namespace pa

@@ -56,6 +56,13 @@ uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 constexpr int64_t kLastLevelCacheBytes = 256ll << 20;
 
 // Host-visible argument checks shared by every entry point.
+// Packed rows (G * max_query_len) one call may carry per KV head: mixed
+// batches of prefill chunks and decode rows, in blocks of 16 to 64 rows.
+constexpr int kMaxRows = 1024;
+
+// Head dims with matrix-core kernels (whole 32-dim k-steps, instantiated).
+bool mfma_head_dim(int D) { return D == 64 || D == 128 || D == 256; }
+
 pa_status check_shape(const pa_dims* d, int32_t window, int32_t num_kv_heads, int32_t block_size) {
   if (!d) return fail(PA_ERR_INVALID_ARG, "dims is NULL");
   if (d->batch < 0 || d->batch > 65535)
@@ -66,8 +73,10 @@ pa_status check_shape(const pa_dims* d, int32_t window, int32_t num_kv_heads, in
     return fail(PA_ERR_INVALID_ARG, "kv_format %d unknown", d->kv_format);
   if (d->kv_format == PA_KV_FP8_E4M3 && d->dtype != PA_BF16)
     return fail(PA_ERR_UNSUPPORTED, "an FP8 KV cache needs bf16 q and out");
-  if (d->head_dim != 64 && d->head_dim != 128)
-    return fail(PA_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", d->head_dim);
+  if (d->head_dim < 1 || d->head_dim > pa::kValuMaxD)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d outside [1, %d]", d->head_dim, pa::kValuMaxD);
+  if (d->kv_format == PA_KV_FP8_E4M3 && !mfma_head_dim(d->head_dim))
+    return fail(PA_ERR_UNSUPPORTED, "an FP8 KV cache needs head_dim 64, 128 or 256");
   if (num_kv_heads < 1 || num_kv_heads > 65535)
     return fail(PA_ERR_INVALID_ARG, "num_kv_heads %d outside [1, 65535]", num_kv_heads);
   if (d->num_q_heads < 1 || d->num_q_heads % num_kv_heads)
@@ -85,9 +94,9 @@ pa_status check_shape(const pa_dims* d, int32_t window, int32_t num_kv_heads, in
                 d->max_blocks_per_seq, d->max_seq_len, block_size);
   if (d->num_blocks < 1) return fail(PA_ERR_INVALID_ARG, "num_blocks %d < 1", d->num_blocks);
   const int64_t rows = (int64_t)(d->num_q_heads / num_kv_heads) * d->max_query_len;
-  if (rows > 64)
-    return fail(PA_ERR_UNSUPPORTED, "rows per KV head G*max_query_len = %lld exceeds 64",
-                (long long)rows);
+  if (rows > kMaxRows)
+    return fail(PA_ERR_UNSUPPORTED, "rows per KV head G*max_query_len = %lld exceeds %d",
+                (long long)rows, kMaxRows);
   return PA_OK;
 }
 
@@ -108,29 +117,39 @@ pa_status make_plan(const pa_dims* d, int32_t window, int32_t hkv, int32_t bs, i
   if (path_req == PA_PATH_AUTO) {
     // fp32 inputs never take reduced-precision products.  For bf16 the matrix
     // cores are faster than the vector kernel at every row count measured on
-    // MI355X (R = 4 included).
-    r.path = d->dtype == PA_F32 ? PA_PATH_VALU : PA_PATH_MFMA;
+    // MI355X (R = 4 included); other head dims take the vector kernel.
+    r.path = (d->dtype == PA_F32 || !mfma_head_dim(d->head_dim)) ? PA_PATH_VALU : PA_PATH_MFMA;
   } else {
     r.path = path_req;
   }
   if (r.path == PA_PATH_MFMA && d->dtype != PA_BF16)
     return fail(PA_ERR_UNSUPPORTED, "the matrix-core path needs bf16 inputs");
+  if (r.path == PA_PATH_MFMA && !mfma_head_dim(d->head_dim))
+    return fail(PA_ERR_UNSUPPORTED, "the matrix-core path takes head_dim 64, 128 or 256");
   if (r.path != PA_PATH_MFMA && d->kv_format == PA_KV_FP8_E4M3)
     return fail(PA_ERR_UNSUPPORTED, "an FP8 KV cache needs the matrix-core path");
-  const int nrt = (r.rows + 15) / 16;
   if (r.path == PA_PATH_MFMA) {
+    // Row tiles (16 rows each) per workgroup: all rows when they fit in 64
+    // (D = 256: one tile, for registers); beyond that blocks of 64 rows at
+    // D = 64 and 32 rows at D = 128, which keep 3-4 waves per SIMD.
+    const int need = (r.rows + 15) / 16;
+    const int cap = d->head_dim == 256 ? 1 : (r.rows <= 64 ? 4 : (d->head_dim == 64 ? 4 : 2));
+    r.row_tiles = std::min(need, cap);
     const int w_req = o ? o->waves : 0;
     if (w_req) {
       if (w_req != 1 && w_req != 2 && w_req != 4)
         return fail(PA_ERR_INVALID_ARG, "waves %d must be 1, 2 or 4", w_req);
-      if (w_req * nrt > 4)
-        return fail(PA_ERR_UNSUPPORTED, "waves %d x row tiles %d exceeds 4", w_req, nrt);
+      if (w_req * r.row_tiles > 4)
+        return fail(PA_ERR_UNSUPPORTED, "waves %d x row tiles %d exceeds 4", w_req, r.row_tiles);
       r.waves = w_req;
     } else {
-      r.waves = nrt == 1 ? 4 : (nrt == 2 ? 2 : 1);
+      r.waves = r.row_tiles == 1 ? 4 : (r.row_tiles == 2 ? 2 : 1);
     }
+    r.row_blocks = (r.rows + 16 * r.row_tiles - 1) / (16 * r.row_tiles);
   } else {
     r.waves = 4;  // 256-thread workgroup
+    r.row_tiles = pa::kValuRows / 16;
+    r.row_blocks = (r.rows + pa::kValuRows - 1) / pa::kValuRows;
   }
   const int64_t span_cover = (int64_t)r.span_max + pa::kChunk - 1;  // span plus alignment slack
   const int64_t units = (int64_t)d->batch * hkv;
@@ -141,13 +160,15 @@ pa_status make_plan(const pa_dims* d, int32_t window, int32_t hkv, int32_t bs, i
       return fail(PA_ERR_UNSUPPORTED, "the persistent schedule needs the matrix-core path");
     if (d->batch > pa::kPsMaxBatch)
       return fail(PA_ERR_UNSUPPORTED, "the persistent schedule handles batch <= %d", pa::kPsMaxBatch);
+    if (r.row_blocks > 1)
+      return fail(PA_ERR_UNSUPPORTED, "the persistent schedule needs all rows in one workgroup");
   }
   // Persistent schedule (measured on MI355X: +3-5 % on many-unit split
   // shapes, slightly slower for one (sequence, head) or one-shot calls):
   // matrix-core path, at least 64 (sequence, KV head) units, batch that fits
   // its shared-memory prefix sums, and a span long enough to split.
   const bool ps_auto = r.path == PA_PATH_MFMA && units >= 64 && d->batch <= pa::kPsMaxBatch &&
-                       span_cover > 8 * pa::kChunk;
+                       span_cover > 8 * pa::kChunk && r.row_blocks == 1;
   r.persistent = sched_req == 2 ? 1 : (sched_req == 1 ? 0 : (ps_auto ? 1 : 0));
   const int p_req = o ? o->part_size : 0;
   if (p_req) {
@@ -253,6 +274,14 @@ void launch_mfma_inst(dim3 grid, bool persistent, int cus, hipStream_t s, const 
 template <int D, bool STREAM, bool KV8>
 bool launch_mfma_shape(int nrt, int nw, dim3 grid, bool persistent, int cus, hipStream_t s,
                        const pa::PartArgs& a) {
+  if constexpr (D == 256) {  // one row tile (the plan never asks for more)
+    switch (nrt * 8 + nw) {
+      case 1 * 8 + 1: launch_mfma_inst<D, 1, 1, STREAM, KV8>(grid, persistent, cus, s, a); return true;
+      case 1 * 8 + 2: launch_mfma_inst<D, 1, 2, STREAM, KV8>(grid, persistent, cus, s, a); return true;
+      case 1 * 8 + 4: launch_mfma_inst<D, 1, 4, STREAM, KV8>(grid, persistent, cus, s, a); return true;
+      default: return false;
+    }
+  } else {
   switch (nrt * 8 + nw) {
     case 1 * 8 + 1: launch_mfma_inst<D, 1, 1, STREAM, KV8>(grid, persistent, cus, s, a); return true;
     case 1 * 8 + 2: launch_mfma_inst<D, 1, 2, STREAM, KV8>(grid, persistent, cus, s, a); return true;
@@ -262,6 +291,7 @@ bool launch_mfma_shape(int nrt, int nw, dim3 grid, bool persistent, int cus, hip
     case 3 * 8 + 1: launch_mfma_inst<D, 3, 1, STREAM, KV8>(grid, persistent, cus, s, a); return true;
     case 4 * 8 + 1: launch_mfma_inst<D, 4, 1, STREAM, KV8>(grid, persistent, cus, s, a); return true;
     default: return false;
+  }
   }
 }
 
@@ -347,6 +377,8 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
   a.batch = d->batch;
   a.k_scale = kv8 ? o->k_scale : nullptr;
   a.v_scale = kv8 ? o->v_scale : nullptr;
+  a.row_blocks = p.row_blocks;
+  a.head_dim = d->head_dim;
 
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
@@ -354,21 +386,21 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
     e = hipEventRecord((hipEvent_t)o->event_begin, s);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord(begin)");
   }
-  const uint64_t nwg = (uint64_t)p.num_parts * hkv * d->batch;
+  const uint64_t nwg = (uint64_t)p.num_parts * hkv * d->batch * p.row_blocks;
   if (nwg > 0x7fffffffull) return fail(PA_ERR_UNSUPPORTED, "grid of %llu workgroups too large", (unsigned long long)nwg);
   const dim3 grid((uint32_t)nwg);
-  const int nrt = (p.rows + 15) / 16;
+  const int nrt = p.row_tiles;
   bool ok = true;
   if (p.path == PA_PATH_MFMA) {
-    ok = d->head_dim == 64
-             ? launch_mfma<64>(nrt, p.waves, grid, p.persistent, p.streaming, kv8, cus, s, a)
-             : launch_mfma<128>(nrt, p.waves, grid, p.persistent, p.streaming, kv8, cus, s, a);
+    switch (d->head_dim) {
+      case 64: ok = launch_mfma<64>(nrt, p.waves, grid, p.persistent, p.streaming, kv8, cus, s, a); break;
+      case 128: ok = launch_mfma<128>(nrt, p.waves, grid, p.persistent, p.streaming, kv8, cus, s, a); break;
+      default: ok = launch_mfma<256>(nrt, p.waves, grid, p.persistent, p.streaming, kv8, cus, s, a); break;
+    }
   } else if (d->dtype == PA_F32) {
-    if (d->head_dim == 64) hipLaunchKernelGGL((pa::part_valu<float, 64>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((pa::part_valu<float, 128>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((pa::part_valu<float>), grid, dim3(256), 0, s, a);
   } else {
-    if (d->head_dim == 64) hipLaunchKernelGGL((pa::part_valu<uint16_t, 64>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((pa::part_valu<uint16_t, 128>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((pa::part_valu<uint16_t>), grid, dim3(256), 0, s, a);
   }
   if (!ok) return fail(PA_ERR_UNSUPPORTED, "no kernel for %d row tiles x %d waves", nrt, p.waves);
   e = hipGetLastError();
@@ -393,20 +425,22 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
     r.rows = p.rows;
     r.num_parts = p.num_parts;
     r.part_size = p.part_size;
+    r.head_dim = d->head_dim;
     // persistent: a unit has about one state per workgroup share it crosses
     const int gp = pa::reduce_group_lanes(p.persistent ? std::min(p.num_parts, 32) : p.num_parts);
-    const int units = p.rows * (d->head_dim / 4);
+    const int vec = d->head_dim % 4 == 0 ? 4 : 1;  // dims per merge unit
+    const int units = p.rows * (d->head_dim / vec);
     const dim3 rgrid((units + 256 / gp - 1) / (256 / gp), hkv, d->batch);
-#define PA_REDUCE(T, D)                                                                     \
+#define PA_REDUCE(T, V)                                                                     \
   switch (gp) {                                                                            \
-    case 1: hipLaunchKernelGGL((pa::lse_reduce<T, D, 1>), rgrid, dim3(256), 0, s, r); break; \
-    case 16: hipLaunchKernelGGL((pa::lse_reduce<T, D, 16>), rgrid, dim3(256), 0, s, r); break; \
-    default: hipLaunchKernelGGL((pa::lse_reduce<T, D, 256>), rgrid, dim3(256), 0, s, r); break; \
+    case 1: hipLaunchKernelGGL((pa::lse_reduce<T, V, 1>), rgrid, dim3(256), 0, s, r); break; \
+    case 16: hipLaunchKernelGGL((pa::lse_reduce<T, V, 16>), rgrid, dim3(256), 0, s, r); break; \
+    default: hipLaunchKernelGGL((pa::lse_reduce<T, V, 256>), rgrid, dim3(256), 0, s, r); break; \
   }
     if (d->dtype == PA_F32) {
-      if (d->head_dim == 64) { PA_REDUCE(float, 64) } else { PA_REDUCE(float, 128) }
+      if (vec == 4) { PA_REDUCE(float, 4) } else { PA_REDUCE(float, 1) }
     } else {
-      if (d->head_dim == 64) { PA_REDUCE(uint16_t, 64) } else { PA_REDUCE(uint16_t, 128) }
+      if (vec == 4) { PA_REDUCE(uint16_t, 4) } else { PA_REDUCE(uint16_t, 1) }
     }
 #undef PA_REDUCE
     e = hipGetLastError();

@@ -97,7 +97,7 @@ struct ChunkBlocks {
 template <int D, int NRT, int NW, bool STREAM, bool KV8>
 __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L, int q, int qoff,
                                          const SeqView& sv, int j_first, int j_last, int slot,
-                                         bool write_out) {
+                                         bool write_out, int r0 = 0) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   constexpr int ES = KV8 ? 1 : 2;        // bytes per cached element
@@ -126,7 +126,7 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
   bf16x8 qf[NRT][KS];
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
-    const int n = rt * 16 + ln;
+    const int n = r0 + rt * 16 + ln;
     if (n < rows_b) {
       const int i = n / G;
       const int g = n - i * G;
@@ -366,7 +366,7 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
     if (wave == 0) {
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) {
-        const int n = rt * 16 + ln;
+        const int n = rt * 16 + ln;  // row within the block (shared-memory index)
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][n]);
@@ -392,7 +392,7 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
     const bool one_shot = write_out;
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
-      const int n = rt * 16 + ln;
+      const int n = r0 + rt * 16 + ln;
       if (n >= rows_b) continue;
       const float inv = lrun[rt] > 0.f ? v_scale / lrun[rt] : 0.f;
       if (one_shot) {
@@ -429,8 +429,11 @@ __global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
   const int q = a.query_lens[it.b];
   const SeqView sv = seq_view(L, q, a.window, a.part_size);
   if (it.j >= sv.nparts) return;  // empty partition: contributes nothing
+  const int r0 = it.rb * 16 * NRT;                // first packed row of this block
+  if (r0 >= a.group * q) return;                 // no row of this sequence is in it
   const int qoff = wave_row_offset(a.query_lens, it.b);
-  mfma_run<D, NRT, NW, STREAM, KV8>(a, it.b, it.h, L, q, qoff, sv, it.j, it.j, it.j, sv.nparts == 1);
+  mfma_run<D, NRT, NW, STREAM, KV8>(a, it.b, it.h, L, q, qoff, sv, it.j, it.j, it.j, sv.nparts == 1,
+                                    r0);
 }
 
 // Persistent schedule (aiter PR #2914: "PS" decode): a grid of about one

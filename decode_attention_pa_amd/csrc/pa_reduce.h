@@ -17,7 +17,7 @@
 
 namespace pa {
 
-// One thread group per output unit = (packed row n, 4 consecutive dims) of
+// One thread group per output unit = (packed row n, VEC consecutive dims) of
 // one (sequence, KV head); the GP threads of a group split the partitions
 // (GP = 1, 16 or 256, chosen on the host from NP) and combine their partial
 // sums by a fixed butterfly / tree, so results are deterministic.  Each
@@ -61,10 +61,14 @@ struct GroupReduce {
   }
 };
 
-template <typename T, int D, int GP>
+// VEC = 4: a unit is 4 consecutive dims (head dims divisible by 4); VEC = 1:
+// one dim.  The head dim itself is a run-time value.
+template <typename T, int VEC, int GP>
 __global__ __launch_bounds__(256) void lse_reduce(ReduceArgs a) {
+  typedef float fvec __attribute__((ext_vector_type(VEC)));
   constexpr int UPW = 256 / GP;  // units per workgroup
-  constexpr int D4 = D / 4;
+  const int D = a.head_dim;
+  const int D4 = D / VEC;        // units per row
   constexpr int U = 4;           // partitions in flight per thread per step
   __shared__ float lds[4];
   const int h = blockIdx.y, b = blockIdx.z;
@@ -89,25 +93,25 @@ __global__ __launch_bounds__(256) void lse_reduce(ReduceArgs a) {
   // partitions (rescaling its sums when it grows), then the group agrees on
   // M = max mt and every thread rescales by 2^(mt - M) before the sums.
   float mt = -INFINITY;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  fvec acc = {};
   float den = 0.f;
   for (int j0 = gp; j0 < np; j0 += GP * U) {
     // Every slot below np was written by this call's partition kernel, with
     // finite values (a row that saw nothing stores m = -inf, l = 0, o = 0),
     // so all three are requested together: one round trip per step.
     float mj[U], lj[U];
-    f32x4 o[U];
+    fvec o[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int jj = j0 + u * GP;
       mj[u] = -INFINITY;
       lj[u] = 0.f;
-      o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      o[u] = fvec{};
       if (jj < np) {
         const size_t w = (base + jj) * a.rows + n;
         mj[u] = a.ws_m[w];
         lj[u] = a.ws_l[w];
-        o[u] = *(const f32x4*)(a.ws_o + w * D + d4 * 4);
+        o[u] = *(const fvec*)(a.ws_o + w * D + d4 * VEC);
       }
     }
 #pragma unroll
@@ -129,36 +133,40 @@ __global__ __launch_bounds__(256) void lse_reduce(ReduceArgs a) {
   acc *= r;
   den *= r;
   if constexpr (GP == 256) {
-    // the whole workgroup is one group: reduce the five sums per wave, then
-    // once through shared memory
-    __shared__ float part[4][5];
-    float v[5] = {acc[0], acc[1], acc[2], acc[3], den};
+    // the whole workgroup is one group: reduce the VEC + 1 sums per wave,
+    // then once through shared memory
+    __shared__ float part[4][VEC + 1];
+    float v[VEC + 1];
 #pragma unroll
-    for (int e = 0; e < 5; ++e) {
+    for (int e = 0; e < VEC; ++e) v[e] = acc[e];
+    v[VEC] = den;
+#pragma unroll
+    for (int e = 0; e <= VEC; ++e) {
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) v[e] += __shfl_xor(v[e], off);
     }
     const int wave = tid >> 6;
     if ((tid & 63) == 0) {
 #pragma unroll
-      for (int e = 0; e < 5; ++e) part[wave][e] = v[e];
+      for (int e = 0; e <= VEC; ++e) part[wave][e] = v[e];
     }
     __syncthreads();
 #pragma unroll
-    for (int e = 0; e < 5; ++e) v[e] = ((part[0][e] + part[1][e]) + part[2][e]) + part[3][e];
-    acc = f32x4{v[0], v[1], v[2], v[3]};
-    den = v[4];
+    for (int e = 0; e <= VEC; ++e) v[e] = ((part[0][e] + part[1][e]) + part[2][e]) + part[3][e];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = v[e];
+    den = v[VEC];
   } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = GroupReduce<GP>::sum(acc[e], lds);
+    for (int e = 0; e < VEC; ++e) acc[e] = GroupReduce<GP>::sum(acc[e], lds);
     den = GroupReduce<GP>::sum(den, lds);
   }
   if (gp != 0) return;
   const float inv = den > 0.f ? 1.f / den : 0.f;
   const int i = n / G, g = n - i * G;
-  T* op = (T*)a.out + ((size_t)(qoff + i) * a.num_q_heads + (size_t)h * G + g) * D + d4 * 4;
+  T* op = (T*)a.out + ((size_t)(qoff + i) * a.num_q_heads + (size_t)h * G + g) * D + d4 * VEC;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) store_elem<T>(op + e, acc[e] * inv);
+  for (int e = 0; e < VEC; ++e) store_elem<T>(op + e, acc[e] * inv);
 }
 
 // Partition lanes per output unit for a given number of states per unit.

@@ -35,7 +35,9 @@
  *                 8-11, half 1 slots 4-7 and 12-15; each half is a [D/E][8][E]
  *                 tile (column of E dims, place, dim within the column).  For
  *                 bf16 and FP8 a column of one slot is 16 contiguous bytes and a
- *                 column of a half 128
+ *                 column of a half 128.  Head dims that are not a multiple of 8
+ *                 (vector path only) keep one row per slot: [num_blocks, H_kv,
+ *                 block_size, D]
  *   v_cache       [num_blocks, H_kv, block_size/8, D, 8]: slots grouped by 8;
  *                 slot s of a block lives at [s/8][d][s%8] (a [D, 8] tile per
  *                 group: 16 contiguous bytes hold one dim of 8 consecutive
@@ -102,7 +104,8 @@ typedef enum pa_kv_format {
 typedef struct pa_dims {
   int32_t batch;              /* B >= 0 */
   int32_t num_q_heads;        /* H_q, a multiple of num_kv_heads */
-  int32_t head_dim;           /* D: 64 or 128 */
+  int32_t head_dim;           /* D in [1, 256]; the matrix-core path (bf16 and FP8 caches)
+                                 takes 64, 128 and 256, the vector path any D */
   int32_t max_query_len;      /* upper bound on query_lens[b], >= 1 */
   int32_t max_seq_len;        /* upper bound on seq_lens[b], >= 1 */
   int32_t max_blocks_per_seq; /* row stride of block_tables, >= ceil(max_seq_len/block_size) */
@@ -129,6 +132,8 @@ typedef struct pa_plan {
   int32_t one_shot;           /* 1: a single partition writes out directly */
   int32_t persistent;         /* 1: persistent schedule (resident grid, balanced partition
                                  shares); 0: one workgroup per partition */
+  int32_t row_tiles;          /* 16-row tiles of packed rows per workgroup */
+  int32_t row_blocks;         /* workgroups that split the R rows of one partition */
   int32_t streaming;          /* 1: KV loads are non-temporal (the call's KV bound exceeds
                                  the 256 MB last-level cache); 0: cached loads, so a KV
                                  working set that fits stays resident across calls.

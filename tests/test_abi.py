@@ -107,7 +107,7 @@ def test_plan_window_bounds_the_span(lib):
 
 
 BAD = [
-    (dict(head_dim=96), pa.ERR_UNSUPPORTED),
+    (dict(head_dim=257), pa.ERR_UNSUPPORTED),
     (dict(head_dim=0), pa.ERR_UNSUPPORTED),
     (dict(dtype=7), pa.ERR_INVALID_ARG),
     (dict(batch=-1), pa.ERR_INVALID_ARG),
@@ -116,8 +116,39 @@ BAD = [
     (dict(max_seq_len=0), pa.ERR_INVALID_ARG),
     (dict(max_blocks_per_seq=3), pa.ERR_INVALID_ARG),   # 8192 / 16 needs 512
     (dict(num_blocks=0), pa.ERR_INVALID_ARG),
-    (dict(max_query_len=17), pa.ERR_UNSUPPORTED),       # 4 * 17 rows > 64
+    (dict(max_query_len=257), pa.ERR_UNSUPPORTED),      # 4 * 257 rows > 1024
 ]
+
+
+def test_general_rows_and_head_dims(lib):
+    """More than 64 packed rows go in row blocks (16-row tiles: up to 64 rows
+    per workgroup at D = 64, 32 at D = 128, 16 at D = 256, 16 on the vector
+    path); head dims off the matrix-core set take the vector path."""
+    w = workloads.WORKLOADS["gqa_bf16"]
+    p = pa.plan(dims_of(w, max_query_len=17), 0, 8, 16)            # 68 rows, D = 128
+    assert (p["path"], p["row_tiles"], p["row_blocks"], p["waves"]) == (pa.PATH_MFMA, 2, 3, 2)
+    assert p["persistent"] == 0                                      # one block per workgroup only
+    p = pa.plan(dims_of(w, max_query_len=16), 0, 8, 16)             # 64 rows fit one block
+    assert (p["row_tiles"], p["row_blocks"]) == (4, 1)
+    p = pa.plan(dims_of(w, max_query_len=256, head_dim=64), 0, 8, 16)   # 1024 rows
+    assert (p["row_tiles"], p["row_blocks"], p["waves"]) == (4, 16, 1)
+    p = pa.plan(dims_of(w, max_query_len=3, head_dim=256), 0, 8, 16)    # 12 rows, D = 256
+    assert (p["path"], p["row_tiles"], p["row_blocks"], p["waves"]) == (pa.PATH_MFMA, 1, 1, 4)
+    p = pa.plan(dims_of(w, max_query_len=5, head_dim=256), 0, 8, 16)    # 20 rows, D = 256
+    assert (p["row_tiles"], p["row_blocks"]) == (1, 2)
+    p = pa.plan(dims_of(w, head_dim=66), 0, 8, 16)                   # odd head dim
+    assert (p["path"], p["row_tiles"], p["row_blocks"]) == (pa.PATH_VALU, 1, 1)
+    p = pa.plan(dims_of(w, head_dim=66, max_query_len=9), 0, 8, 16)  # 36 rows
+    assert p["row_blocks"] == 3
+    with pytest.raises(pa.PaError) as e:                             # no matrix-core kernel
+        pa.plan(dims_of(w, head_dim=66), 0, 8, 16, path=pa.PATH_MFMA)
+    assert e.value.status == pa.ERR_UNSUPPORTED
+    with pytest.raises(pa.PaError) as e:                             # rows must fit one block
+        pa.plan(dims_of(w, max_query_len=17), 0, 8, 16, schedule=pa.SCHED_PERSISTENT)
+    assert e.value.status == pa.ERR_UNSUPPORTED
+    with pytest.raises(pa.PaError) as e:                             # FP8 needs the matrix cores
+        pa.plan(dims_of(w, head_dim=66, kv_format=pa.KV_FP8_E4M3), 0, 8, 16)
+    assert e.value.status == pa.ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("over,code", BAD)

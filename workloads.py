@@ -105,6 +105,20 @@ WORKLOADS = {
         description="GQA decode, bf16 queries over an FP8 (E4M3) KV cache with "
                     "per-tensor scales: B=32, 32/8 heads, D=128, bs=16, "
                     "context U[512, 8192], q_len 1, window 0"),
+    "qwen_d256_bf16": Workload(
+        name="qwen_d256_bf16", dtype="bf16", batch=1, num_q_heads=16, num_kv_heads=2,
+        head_dim=256, block_size=16, query_len=1, windows=(0,), scale=1.0 / 16.0, seed=6,
+        max_blocks_per_seq=1024, max_seq_len=16384, seq_lens=(16384,), pool=1280,
+        description="head-dim-256 decode bf16 (the split-K decode shape of executorch "
+                    "PR #18759: B=1, 16/2 heads, D=256), bs=16, context 16384, q_len 1"),
+    "prefill_chunk_bf16": Workload(
+        name="prefill_chunk_bf16", dtype="bf16", batch=16, num_q_heads=32, num_kv_heads=4,
+        head_dim=128, block_size=16, query_len=16, windows=(0,),
+        scale=1.0 / math.sqrt(128.0), seed=7, max_blocks_per_seq=512, max_seq_len=8192,
+        len_range=(2048, 8192),
+        description="mixed-batch rows beyond one tile: B=16, 32/4 heads (G=8), D=128, "
+                    "bs=16, 16 query tokens per sequence (128 packed rows per KV head), "
+                    "context U[2048, 8192], window 0"),
     "large_block_mtp_bf16": Workload(
         name="large_block_mtp_bf16", dtype="bf16", batch=128, num_q_heads=64,
         num_kv_heads=8, head_dim=128, block_size=1024, query_len=2, windows=(4096, 0),
