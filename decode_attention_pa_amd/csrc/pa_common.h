@@ -142,13 +142,22 @@ struct PartItem {
   int j, h, b, rb;
 };
 
-// Row blocks of one (partition, sequence, KV head) are the fastest index:
-// they read the same K/V, so they run side by side and share its lines.
+// Row blocks of one (partition, sequence, KV head) read the same K/V.
+// Workgroup ids are dealt to the 8 XCDs round-robin, so the row blocks of a
+// unit take ids 8 apart: all on one XCD, sharing its L2, while 8 units fill
+// the 8 XCDs.  (The grid is padded to whole groups of 8 units; a padded id
+// lands on a partition index >= num_parts and exits.)
+constexpr int kXcds = 8;
 __device__ inline PartItem part_item(const PartArgs& a) {
   const int id = blockIdx.x;
   PartItem it;
-  it.rb = id % a.row_blocks;
-  const int u = id / a.row_blocks;
+  int u = id;
+  it.rb = 0;
+  if (a.row_blocks > 1) {
+    const int rest = id / kXcds;
+    it.rb = rest % a.row_blocks;
+    u = (rest / a.row_blocks) * kXcds + id % kXcds;
+  }
   it.h = u % a.num_kv_heads;
   const int r = u / a.num_kv_heads;
   it.b = r % a.batch;

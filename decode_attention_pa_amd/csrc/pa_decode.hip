@@ -186,12 +186,14 @@ pa_status make_plan(const pa_dims* d, int32_t window, int32_t hkv, int32_t bs, i
     r.part_size = (int32_t)(pc * pa::kChunk);
   } else {
     // Enough partitions for ~8 workgroups per CU if every (sequence, KV
-    // head) had the longest span (real batches average less), with
-    // partitions of 8..128 chunks: longer ones amortise each workgroup's
-    // set-up and keep the partial states small, shorter ones would
-    // multiply the LSE merge's work.  Constants measured on MI355X.
+    // head) had the longest span (real batches average less), counting
+    // each row block as a workgroup, with partitions of 8..128 chunks:
+    // longer ones amortise each workgroup's set-up and keep the partial
+    // states small, shorter ones would multiply the LSE merge's work.
+    // Constants measured on MI355X.
     const int64_t chunks = cdiv(span_cover, pa::kChunk);
-    const int64_t want = std::max<int64_t>(1, cdiv(8 * (int64_t)num_cus, std::max<int64_t>(units, 1)));
+    const int64_t wgs_per_part = std::max<int64_t>(units * r.row_blocks, 1);
+    const int64_t want = std::max<int64_t>(1, cdiv(8 * (int64_t)num_cus, wgs_per_part));
     int64_t pc = cdiv(chunks, want);
     pc = std::max<int64_t>(pc, 8);
     pc = std::min<int64_t>(pc, 128);
@@ -386,7 +388,10 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
     e = hipEventRecord((hipEvent_t)o->event_begin, s);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord(begin)");
   }
-  const uint64_t nwg = (uint64_t)p.num_parts * hkv * d->batch * p.row_blocks;
+  const uint64_t units = (uint64_t)p.num_parts * hkv * d->batch;  // (partition, seq, head)
+  const uint64_t nwg = p.row_blocks > 1
+                           ? (units + pa::kXcds - 1) / pa::kXcds * pa::kXcds * p.row_blocks
+                           : units;
   if (nwg > 0x7fffffffull) return fail(PA_ERR_UNSUPPORTED, "grid of %llu workgroups too large", (unsigned long long)nwg);
   const dim3 grid((uint32_t)nwg);
   const int nrt = p.row_tiles;
