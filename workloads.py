@@ -23,7 +23,7 @@ Layouts (the library's contract):
     seq_lens      int32 [B]  (context length, query tokens included)
     query_lens    int32 [B]
 
-Recipe (also in the design doc): lengths and block tables come from a CPU
+Recipe: lengths and block tables come from a CPU
 ``torch.Generator`` seeded with the workload's seed; the pool holds
 ceil(1.25 x needed) blocks unless the workload fixes it, and a seeded random
 permutation of the pool is dealt out to the sequences in order.  Table
@@ -105,12 +105,13 @@ WORKLOADS = {
         description="GQA decode, bf16 queries over an FP8 (E4M3) KV cache with "
                     "per-tensor scales: B=32, 32/8 heads, D=128, bs=16, "
                     "context U[512, 8192], q_len 1, window 0"),
-    "qwen_d256_bf16": Workload(
-        name="qwen_d256_bf16", dtype="bf16", batch=1, num_q_heads=16, num_kv_heads=2,
+    "d256_decode_bf16": Workload(
+        name="d256_decode_bf16", dtype="bf16", batch=1, num_q_heads=16, num_kv_heads=2,
         head_dim=256, block_size=16, query_len=1, windows=(0,), scale=1.0 / 16.0, seed=6,
         max_blocks_per_seq=1024, max_seq_len=16384, seq_lens=(16384,), pool=1280,
-        description="head-dim-256 decode bf16 (the split-K decode shape of executorch "
-                    "PR #18759: B=1, 16/2 heads, D=256), bs=16, context 16384, q_len 1"),
+        description="head-dim-256 decode bf16 (the split-K decode benchmark shape of "
+                    "executorch PR #18759: B=1, 16/2 heads, D=256), bs=16, context 16384, "
+                    "q_len 1"),
     "prefill_chunk_bf16": Workload(
         name="prefill_chunk_bf16", dtype="bf16", batch=16, num_q_heads=32, num_kv_heads=4,
         head_dim=128, block_size=16, query_len=16, windows=(0,),
