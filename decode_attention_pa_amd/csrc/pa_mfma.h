@@ -115,6 +115,12 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
   const int bs_mask = (1 << log2_bs) - 1;
 
   const int32_t* __restrict__ table = a.block_tables + (size_t)b * a.max_blocks_per_seq;
+  // The block table is read-only for the whole call: through the constant
+  // address space, uniform indices become scalar loads (their own wait
+  // counter).  As vector loads, waiting for a block id would also wait for
+  // the K/V loads issued before it and drain the pipeline every chunk.
+  const __attribute__((address_space(4))) int32_t* stable =
+      (const __attribute__((address_space(4))) int32_t*)table;
   const uint8_t* __restrict__ kc = (const uint8_t*)a.k_cache;
   const uint8_t* __restrict__ vc = (const uint8_t*)a.v_cache;
   const size_t slab = ((size_t)D * ES) << log2_bs;          // bytes per (block, head)
@@ -158,8 +164,8 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
     ChunkBlocks cb;
     cb.first_idx = __builtin_amdgcn_readfirstlane(lo >> log2_bs);
     const int second_idx = __builtin_amdgcn_readfirstlane(hi >> log2_bs);
-    cb.first = __builtin_amdgcn_readfirstlane(table[cb.first_idx]);
-    cb.second = __builtin_amdgcn_readfirstlane(table[second_idx]);
+    cb.first = stable[cb.first_idx];
+    cb.second = stable[second_idx];
     return cb;
   };
   // K rows: lane (ln, lg) of tile t holds position 8*(ln/4) + 4*t + ln%4 of
