@@ -70,6 +70,9 @@ def algorithmic_bytes(case) -> dict:
                 partition_kernel=kv + qb + tables + lens)
 
 
+CALIB_COPIES = 3  # plain 1 GiB device copies issued by --copy-calibration
+
+
 def load_traffic(workload: str, window: int):
     """HBM traffic of the partition kernel from the committed rocprofv3 counter
     record, or None if absent or taken on different kernel sources."""
@@ -101,15 +104,15 @@ def ingest_counters(workload: str, window: int, fetch_dir: str, write_dir: str,
     rec = {"workload": workload, "window": window, "kernel_hash": kernel_source_hash(),
            "command": command}
     for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        copy, part = [], []
-        for r in _counter_rows(d):
-            if r["Counter_Name"] != name:
-                continue
-            v = float(r["Counter_Value"])
-            if "copyBuffer" in r["Kernel_Name"] and v > gib_kib / 8:
-                copy.append(v)
-            elif "part_mfma" in r["Kernel_Name"] or "part_valu" in r["Kernel_Name"]:
-                part.append(v)
+        rows = sorted(((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"]))
+                       for r in _counter_rows(d) if r["Counter_Name"] == name))
+        part = [v for _, k, v in rows if "part_mfma" in k or "part_valu" in k]
+        first_part = min((i for i, k, _ in rows if "part_mfma" in k or "part_valu" in k), default=0)
+        # the calibration copies are the last CALIB_COPIES large copies before
+        # the first partition kernel; earlier ones stage the workload's inputs
+        # (of other sizes) and would skew the scale
+        copy = [v for i, k, v in rows
+                if "copyBuffer" in k and v > gib_kib / 8 and i < first_part][-CALIB_COPIES:]
         if not copy or not part:
             raise SystemExit(f"{name}: no calibration copy or partition kernel in {d}")
         calib = sum(copy) / len(copy)
@@ -229,7 +232,7 @@ def main(argv=None):
     if a.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
-        for _ in range(3):
+        for _ in range(CALIB_COPIES):
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
