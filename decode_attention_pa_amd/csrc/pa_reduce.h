@@ -17,46 +17,35 @@
 
 namespace pa {
 
-// One thread group per output unit = (packed row n, VEC consecutive dims) of
-// one (sequence, KV head); the GP threads of a group split the partitions
-// (GP = 1, 16 or 256, chosen on the host from NP) and combine their partial
-// sums by a fixed butterfly / tree, so results are deterministic.  Each
-// thread requests all of its partitions' states before using them.
-// Grid: x = unit blocks of 256/GP units, y = KV head, z = sequence.
+// Output unit = (packed row n, VEC consecutive dims) of one (sequence, KV
+// head).  A 256-thread workgroup covers UPW = 256 / GP consecutive units,
+// and GP lanes split each unit's partitions (GP = 1, 16 or 32, chosen on the
+// host from the state count).  Lane t takes unit t % UPW and partition
+// offset t / UPW: neighbouring lanes read neighbouring dims of one partition
+// state (UPW * VEC * 4 >= 128 bytes, whole cache lines), and a workgroup's
+// lines belong to it alone.  Each thread requests U partitions' states
+// before using any.  The GP partial results of a unit are combined by
+// a fixed xor butterfly inside each wave, then across the 4 waves through
+// shared memory in wave order: results are deterministic.
+// Grid: x = unit blocks of UPW units, y = KV head, z = sequence.
 template <int GP>
 struct GroupReduce {
-  // max and sum over the GP threads of a group (all lanes of the group are
-  // active together: they share one output row)
-  __device__ static float max(float x, float* lds) {
-    if constexpr (GP == 1) return x;
-    if constexpr (GP <= 64) {
-#pragma unroll
-      for (int off = GP / 2; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  static constexpr int UPW = 256 / GP;
+  // GP = 1: nothing to combine.  GP > 1: a unit's lanes are the lanes with
+  // the same lane % UPW in all 4 waves (UPW divides 64).
+  template <typename F>
+  __device__ static float all(float x, float (*lds)[64], F op) {
+    if constexpr (GP == 1) {
       return x;
     } else {
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-      const int wave = threadIdx.x >> 6;
+      for (int off = UPW; off < 64; off <<= 1) x = op(x, __shfl_xor(x, off));
+      const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+      __syncthreads();  // the previous use of lds is finished
+      if (lane < UPW) lds[wave][lane] = x;
       __syncthreads();
-      if ((threadIdx.x & 63) == 0) lds[wave] = x;
-      __syncthreads();
-      return fmaxf(fmaxf(lds[0], lds[1]), fmaxf(lds[2], lds[3]));
-    }
-  }
-  __device__ static float sum(float x, float* lds) {
-    if constexpr (GP == 1) return x;
-    if constexpr (GP <= 64) {
-#pragma unroll
-      for (int off = GP / 2; off > 0; off >>= 1) x += __shfl_xor(x, off);
-      return x;
-    } else {
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-      const int wave = threadIdx.x >> 6;
-      __syncthreads();
-      if ((threadIdx.x & 63) == 0) lds[wave] = x;
-      __syncthreads();
-      return ((lds[0] + lds[1]) + lds[2]) + lds[3];
+      const int u = lane % UPW;
+      return op(op(op(lds[0][u], lds[1][u]), lds[2][u]), lds[3][u]);
     }
   }
 };
@@ -66,11 +55,11 @@ struct GroupReduce {
 template <typename T, int VEC, int GP>
 __global__ __launch_bounds__(256) void lse_reduce(ReduceArgs a) {
   typedef float fvec __attribute__((ext_vector_type(VEC)));
-  constexpr int UPW = 256 / GP;  // units per workgroup
+  constexpr int UPW = GroupReduce<GP>::UPW;  // units per workgroup
+  constexpr int U = GP == 1 ? 4 : 16;        // partitions in flight per thread per step
   const int D = a.head_dim;
-  const int D4 = D / VEC;        // units per row
-  constexpr int U = 4;           // partitions in flight per thread per step
-  __shared__ float lds[4];
+  const int D4 = D / VEC;                    // units per row
+  __shared__ float lds[4][64];
   const int h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   // One round of independent loads: lengths, run count, row offset.
@@ -82,11 +71,14 @@ __global__ __launch_bounds__(256) void lse_reduce(ReduceArgs a) {
   const SeqView sv = seq_view(L, q, a.window, a.part_size);
   // states to merge: one per partition, or the unit's run count
   const int np = a.ws_runs ? min(runs, a.num_parts) : (sv.nparts > 1 ? min(sv.nparts, a.num_parts) : 0);
-  if (np <= 0) return;  // the partition kernel wrote these rows directly
-  const int unit = blockIdx.x * UPW + tid / GP;
-  const int gp = tid % GP;
+  if (np <= 0) return;  // the partition kernel wrote these rows directly (whole workgroup)
+  const int unit = blockIdx.x * UPW + tid % UPW;
+  const int gp = tid / UPW;
   const int n = unit / D4, d4 = unit % D4;
-  if (n >= G * q) return;  // whole groups (and, for GP = 256, whole blocks) leave together
+  // Lanes past the last row stay to the end: the combine below synchronises
+  // the workgroup.  With GP = 1 there is no combine and they leave now.
+  const bool live = n < G * q;
+  if (GP == 1 && !live) return;
   const size_t base = ((size_t)b * a.num_kv_heads + h) * a.num_parts;
 
   // One pass: each thread keeps a running reference max mt over its own
@@ -107,7 +99,7 @@ __global__ __launch_bounds__(256) void lse_reduce(ReduceArgs a) {
       mj[u] = -INFINITY;
       lj[u] = 0.f;
       o[u] = fvec{};
-      if (jj < np) {
+      if (live && jj < np) {
         const size_t w = (base + jj) * a.rows + n;
         mj[u] = a.ws_m[w];
         lj[u] = a.ws_l[w];
@@ -128,40 +120,13 @@ __global__ __launch_bounds__(256) void lse_reduce(ReduceArgs a) {
       den += f;
     }
   }
-  const float M = GroupReduce<GP>::max(mt, lds);
+  const float M = GroupReduce<GP>::all(mt, lds, [](float x, float y) { return fmaxf(x, y); });
   const float r = (mt == -INFINITY) ? 0.f : exp2f(mt - M);
-  acc *= r;
-  den *= r;
-  if constexpr (GP == 256) {
-    // the whole workgroup is one group: reduce the VEC + 1 sums per wave,
-    // then once through shared memory
-    __shared__ float part[4][VEC + 1];
-    float v[VEC + 1];
+  const auto add = [](float x, float y) { return x + y; };
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) v[e] = acc[e];
-    v[VEC] = den;
-#pragma unroll
-    for (int e = 0; e <= VEC; ++e) {
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) v[e] += __shfl_xor(v[e], off);
-    }
-    const int wave = tid >> 6;
-    if ((tid & 63) == 0) {
-#pragma unroll
-      for (int e = 0; e <= VEC; ++e) part[wave][e] = v[e];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e <= VEC; ++e) v[e] = ((part[0][e] + part[1][e]) + part[2][e]) + part[3][e];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[e] = v[e];
-    den = v[VEC];
-  } else {
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[e] = GroupReduce<GP>::sum(acc[e], lds);
-    den = GroupReduce<GP>::sum(den, lds);
-  }
-  if (gp != 0) return;
+  for (int e = 0; e < VEC; ++e) acc[e] = GroupReduce<GP>::all(acc[e] * r, lds, add);
+  den = GroupReduce<GP>::all(den * r, lds, add);
+  if (gp != 0 || !live) return;
   const float inv = den > 0.f ? 1.f / den : 0.f;
   const int i = n / G, g = n - i * G;
   T* op = (T*)a.out + ((size_t)(qoff + i) * a.num_q_heads + (size_t)h * G + g) * D + d4 * VEC;
@@ -171,7 +136,7 @@ __global__ __launch_bounds__(256) void lse_reduce(ReduceArgs a) {
 
 // Partition lanes per output unit for a given number of states per unit.
 inline int reduce_group_lanes(int num_states) {
-  return num_states <= 32 ? 1 : (num_states <= 256 ? 16 : 256);
+  return num_states <= 32 ? 1 : (num_states <= 256 ? 16 : 32);
 }
 
 struct SpanArgs {

@@ -134,10 +134,10 @@ typedef struct pa_plan {
                                  shares); 0: one workgroup per partition */
   int32_t row_tiles;          /* 16-row tiles of packed rows per workgroup */
   int32_t row_blocks;         /* workgroups that split the R rows of one partition */
-  int32_t streaming;          /* 1: KV loads are non-temporal (the call's KV bound exceeds
-                                 the 256 MB last-level cache); 0: cached loads, so a KV
-                                 working set that fits stays resident across calls.
-                                 Matrix-core path only (0 on the vector path) */
+  int32_t streaming;          /* 1: KV loads are non-temporal (each K/V byte is read by one
+                                 workgroup); 0: cached loads (row blocks share K/V through
+                                 L2, or forced).  Matrix-core path only (0 on the vector
+                                 path) */
   uint64_t workspace_bytes;   /* bytes pa_decode needs in `workspace` (0 if one_shot) */
 } pa_plan;
 
@@ -149,8 +149,9 @@ typedef struct pa_options {
   int32_t schedule;           /* 0 = auto, 1 = one workgroup per partition, 2 = persistent
                                  (matrix-core path, batch <= 1024) */
   int32_t loads;              /* KV loads on the matrix-core path: 0 = auto (non-temporal
-                                 when min(B * span_max, num_blocks * block_size) positions
-                                 of K and V exceed 256 MB), 1 = cached, 2 = non-temporal */
+                                 unless row blocks re-read K/V), 1 = cached (for callers
+                                 whose KV stays in the 256 MB last-level cache from one
+                                 call to the next), 2 = non-temporal */
   void* event_begin;          /* hipEvent_t recorded on the stream just before the
                                  partition kernel, or NULL */
   void* event_end;            /* hipEvent_t recorded just after it, or NULL */

@@ -197,27 +197,24 @@ def test_persistent_schedule_choice(lib):
 
 
 def test_streaming_loads_choice(lib):
-    # Non-temporal KV loads when min(B * span_max, pool positions) x H_kv x D
-    # x 2 (K and V) x 2 bytes exceeds the 256 MB last-level cache.
-    gqa = workloads.WORKLOADS["gqa_bf16"]            # pool of 10899 blocks: 681 MiB
-    assert pa.plan(dims_of(gqa, num_blocks=10899), 0, 8, 16)["streaming"] == 1
+    # Non-temporal KV loads on the matrix-core path unless row blocks re-read
+    # K/V within the call; the options force either form.
+    gqa = workloads.WORKLOADS["gqa_bf16"]
+    for nb in (10899, 2000):                          # pool size does not matter
+        assert pa.plan(dims_of(gqa, num_blocks=nb), 0, 8, 16)["streaming"] == 1
     assert pa.plan(dims_of(gqa, num_blocks=10899), 0, 8, 16,
                    loads=pa.LOADS_CACHED)["streaming"] == 0
-    # the same shape over a small pool: 2000 x 16 positions x 4 KiB = 125 MiB
-    assert pa.plan(dims_of(gqa, num_blocks=2000), 0, 8, 16)["streaming"] == 0
-    # the bound is strict: exactly 256 MB stays cached, one block more streams
-    per_pos = 8 * 128 * 2 * 2
-    nb = (256 << 20) // (per_pos * 16)
-    assert pa.plan(dims_of(gqa, num_blocks=nb), 0, 8, 16)["streaming"] == 0
-    assert pa.plan(dims_of(gqa, num_blocks=nb + 1), 0, 8, 16)["streaming"] == 1
-    long = workloads.WORKLOADS["long_splitk_bf16"]   # 131072 x 512 B = 64 MiB
-    assert pa.plan(dims_of(long, num_blocks=10240), 0, 1, 16)["streaming"] == 0
+    long = workloads.WORKLOADS["long_splitk_bf16"]
+    assert pa.plan(dims_of(long, num_blocks=10240), 0, 1, 16)["streaming"] == 1
     assert pa.plan(dims_of(long, num_blocks=10240), 0, 1, 16,
-                   loads=pa.LOADS_STREAMING)["streaming"] == 1
-    swa = workloads.WORKLOADS["swa_mtp_bf16"]        # the window bounds the span
-    assert pa.plan(dims_of(swa), 128, 8, 64)["streaming"] == 0
-    big = workloads.WORKLOADS["large_block_mtp_bf16"]
-    assert pa.plan(dims_of(big), 4096, 8, 1024)["streaming"] == 1
+                   loads=pa.LOADS_CACHED)["streaming"] == 0
+    swa = workloads.WORKLOADS["swa_mtp_bf16"]         # 32 rows: two tiles, one block
+    p = pa.plan(dims_of(swa), 128, 8, 64)
+    assert (p["row_blocks"], p["streaming"]) == (1, 1)
+    pre = workloads.WORKLOADS["prefill_chunk_bf16"]   # 128 rows: four row blocks share K/V
+    p = pa.plan(dims_of(pre), 0, 4, 16)
+    assert p["row_blocks"] > 1 and p["streaming"] == 0
+    assert pa.plan(dims_of(pre), 0, 4, 16, loads=pa.LOADS_STREAMING)["streaming"] == 1
     tiny = workloads.WORKLOADS["tiny_f32"]           # vector path: always cached
     assert pa.plan(dims_of(tiny), 0, 1, 16, loads=pa.LOADS_STREAMING)["streaming"] == 0
 
@@ -273,13 +270,10 @@ def test_fp8_kv_format_rules(lib):
         with pytest.raises(pa.PaError) as e:
             pa.plan(dims_of(w, **over), 0, 8, 16, **kw)
         assert e.value.status == code, over
-    # the load form follows the KV bytes: one byte per element halves them
-    big = dims_of(w, num_blocks=10899, kv_format=pa.KV_FP8_E4M3)      # 341 MiB of FP8
-    assert pa.plan(big, 0, 8, 16)["streaming"] == 1
-    half = dims_of(w, num_blocks=6000, kv_format=pa.KV_FP8_E4M3)      # 188 MiB of FP8
-    assert pa.plan(half, 0, 8, 16)["streaming"] == 0
-    native = dims_of(w, num_blocks=6000, kv_format=pa.KV_NATIVE)        # 375 MiB of bf16
-    assert pa.plan(native, 0, 8, 16)["streaming"] == 1
+    # FP8 K/V takes the same load forms
+    fp8 = dims_of(w, num_blocks=6000, kv_format=pa.KV_FP8_E4M3)
+    assert pa.plan(fp8, 0, 8, 16)["streaming"] == 1
+    assert pa.plan(fp8, 0, 8, 16, loads=pa.LOADS_CACHED)["streaming"] == 0
 
 
 def test_empty_batch_is_a_no_op(lib):

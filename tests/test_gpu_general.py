@@ -128,3 +128,26 @@ def test_vector_kernel_nan_poison(D, dtype):
             dirty = run_gpu(workloads.make_case(w, device="cuda", window=win, poison=True),
                             part_size=P)
             assert torch.equal(clean, dirty), (D, dtype, win, P)
+
+
+MERGE_ODD = [(66, "bf16"), (200, "f32")]
+
+
+@pytest.mark.parametrize("D,dtype", MERGE_ODD, ids=[f"d{d}-{t}" for d, t in MERGE_ODD])
+def test_merge_lanes_with_partial_unit_blocks(D, dtype):
+    """Merges with 16 and 32 lanes per output unit where the unit count per
+    (sequence, KV head), rows x D / VEC, is not a multiple of a workgroup's
+    units: the last workgroup holds lanes past the last row."""
+    w = workloads.custom(
+        name=f"merge_odd_d{D}_{dtype}", dtype=dtype, batch=2, num_q_heads=8, num_kv_heads=2,
+        head_dim=D, block_size=16, query_len=3, query_lens=(3, 2), seq_lens=(9000, 70),
+        max_seq_len=9000, max_blocks_per_seq=563, pool=0, seed=4242,
+        scale=float(1.0 / np.sqrt(D)), windows=(0,))
+    tol = BF16_TOL if dtype == "bf16" else F32_TOL
+    for win in (0, 5000):
+        c = workloads.make_case(w, device="cuda", window=win)
+        exp, rows = oracle_out(c)
+        for P in (32, 64):   # 282 / 141 partitions at window 0: 32- and 16-lane merges
+            say(f"[case] merge odd units D={D} {dtype} w={win} P={P}")
+            compare(run_gpu(c, part_size=P), exp, rows, tol,
+                    f"merge odd D={D} {dtype} w={win} P={P}")

@@ -218,7 +218,7 @@ def test_full_workload(name, window, nsample, sched):
 @pytest.mark.parametrize("sched", [pa.SCHED_GRID, pa.SCHED_PERSISTENT])
 @pytest.mark.parametrize("P", [32, 64, 256, 4096])
 def test_reduce_lane_modes(P, sched):
-    """Partition counts in every regime of the merge kernel (1, 16 or 256
+    """Partition counts in every regime of the merge kernel (1, 16 or 32
     lanes per output unit): 3 sequences of up to 20000 positions."""
     w = small(11, head_dim=128, num_q_heads=16, num_kv_heads=2, query_len=2, batch=3,
               seq_lens=(20000, 4000, 129), block_size=32, max_seq_len=20000,
@@ -238,7 +238,7 @@ def _case_for_reuse():
                                      max_seq_len=9000, max_blocks_per_seq=283), device="cuda")
 
 
-REUSE_PLANS = [dict(part_size=32, schedule=pa.SCHED_GRID),      # 283 partitions: 256-lane merge
+REUSE_PLANS = [dict(part_size=32, schedule=pa.SCHED_GRID),      # 283 partitions: 32-lane merge
                dict(part_size=256, schedule=pa.SCHED_GRID),     # 36 partitions: 16-lane merge
                dict(part_size=512, schedule=pa.SCHED_PERSISTENT),
                dict(schedule=pa.SCHED_PERSISTENT),
