@@ -268,15 +268,15 @@ def main(argv=None):
     total_ms = start.elapsed_time(stop)
     flushed_ms = sorted(fb[i].elapsed_time(fe[i]) for i in range(K)) if fb else []
 
-    # Pass 2: the same K calls with HIP events that the library records on
-    # its stream just before and just after the partition kernel, plus events
-    # around each whole call.
+    # Pass 2: the same K calls with HIP events that the library binds to the
+    # partition kernel's dispatch (stamped with that kernel's own start and
+    # end, as a kernel trace reports it), plus events around each whole call.
     kb = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     ke = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     cb = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     ce = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     for e in kb + ke:
-        e.record(stream)  # creates the HIP events; the library re-records them
+        e.record(stream)  # creates the HIP events; the library re-stamps them
     torch.cuda.synchronize()
     for i in range(K):
         if flush_buf is not None:

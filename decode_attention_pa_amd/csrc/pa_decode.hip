@@ -2,6 +2,7 @@
 // kernel dispatch.  Declarations and the full contract: include/pa_decode.h.
 #include "pa_decode.h"
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -263,36 +264,53 @@ int resident_wgs(const void* fn, int threads, int cus) {
   return cus;
 }
 
+// Stream of a call and the caller's timing events.  With events, the
+// partition kernel is launched through hipExtLaunchKernel, which stamps them
+// with that dispatch's own start and end (the interval a kernel trace
+// reports), not with the times the stream reached two separate markers.
+struct Launch {
+  hipStream_t s;
+  hipEvent_t begin, end;
+};
+
+template <typename K>
+void launch_part(K kernel, dim3 grid, dim3 block, const Launch& L, const pa::PartArgs& a) {
+  if (L.begin || L.end)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, L.s, L.begin, L.end, 0, a);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, L.s, a);
+}
+
 template <int D, int NRT, int NW, bool STREAM, bool KV8>
-void launch_mfma_inst(dim3 grid, bool persistent, int cus, hipStream_t s, const pa::PartArgs& a) {
+void launch_mfma_inst(dim3 grid, bool persistent, int cus, const Launch& L, const pa::PartArgs& a) {
   if (persistent) {
     const void* fn = (const void*)pa::part_mfma_ps<D, NRT, NW, STREAM, KV8>;
     const dim3 pgrid(resident_wgs(fn, 64 * NW, cus));
-    hipLaunchKernelGGL((pa::part_mfma_ps<D, NRT, NW, STREAM, KV8>), pgrid, dim3(64 * NW), 0, s, a);
+    launch_part(pa::part_mfma_ps<D, NRT, NW, STREAM, KV8>, pgrid, dim3(64 * NW), L, a);
   } else {
-    hipLaunchKernelGGL((pa::part_mfma<D, NRT, NW, STREAM, KV8>), grid, dim3(64 * NW), 0, s, a);
+    launch_part(pa::part_mfma<D, NRT, NW, STREAM, KV8>, grid, dim3(64 * NW), L, a);
   }
 }
 
 template <int D, bool STREAM, bool KV8>
-bool launch_mfma_shape(int nrt, int nw, dim3 grid, bool persistent, int cus, hipStream_t s,
+bool launch_mfma_shape(int nrt, int nw, dim3 grid, bool persistent, int cus, const Launch& L,
                        const pa::PartArgs& a) {
   if constexpr (D == 256) {  // one row tile (the plan never asks for more)
     switch (nrt * 8 + nw) {
-      case 1 * 8 + 1: launch_mfma_inst<D, 1, 1, STREAM, KV8>(grid, persistent, cus, s, a); return true;
-      case 1 * 8 + 2: launch_mfma_inst<D, 1, 2, STREAM, KV8>(grid, persistent, cus, s, a); return true;
-      case 1 * 8 + 4: launch_mfma_inst<D, 1, 4, STREAM, KV8>(grid, persistent, cus, s, a); return true;
+      case 1 * 8 + 1: launch_mfma_inst<D, 1, 1, STREAM, KV8>(grid, persistent, cus, L, a); return true;
+      case 1 * 8 + 2: launch_mfma_inst<D, 1, 2, STREAM, KV8>(grid, persistent, cus, L, a); return true;
+      case 1 * 8 + 4: launch_mfma_inst<D, 1, 4, STREAM, KV8>(grid, persistent, cus, L, a); return true;
       default: return false;
     }
   } else {
   switch (nrt * 8 + nw) {
-    case 1 * 8 + 1: launch_mfma_inst<D, 1, 1, STREAM, KV8>(grid, persistent, cus, s, a); return true;
-    case 1 * 8 + 2: launch_mfma_inst<D, 1, 2, STREAM, KV8>(grid, persistent, cus, s, a); return true;
-    case 1 * 8 + 4: launch_mfma_inst<D, 1, 4, STREAM, KV8>(grid, persistent, cus, s, a); return true;
-    case 2 * 8 + 1: launch_mfma_inst<D, 2, 1, STREAM, KV8>(grid, persistent, cus, s, a); return true;
-    case 2 * 8 + 2: launch_mfma_inst<D, 2, 2, STREAM, KV8>(grid, persistent, cus, s, a); return true;
-    case 3 * 8 + 1: launch_mfma_inst<D, 3, 1, STREAM, KV8>(grid, persistent, cus, s, a); return true;
-    case 4 * 8 + 1: launch_mfma_inst<D, 4, 1, STREAM, KV8>(grid, persistent, cus, s, a); return true;
+    case 1 * 8 + 1: launch_mfma_inst<D, 1, 1, STREAM, KV8>(grid, persistent, cus, L, a); return true;
+    case 1 * 8 + 2: launch_mfma_inst<D, 1, 2, STREAM, KV8>(grid, persistent, cus, L, a); return true;
+    case 1 * 8 + 4: launch_mfma_inst<D, 1, 4, STREAM, KV8>(grid, persistent, cus, L, a); return true;
+    case 2 * 8 + 1: launch_mfma_inst<D, 2, 1, STREAM, KV8>(grid, persistent, cus, L, a); return true;
+    case 2 * 8 + 2: launch_mfma_inst<D, 2, 2, STREAM, KV8>(grid, persistent, cus, L, a); return true;
+    case 3 * 8 + 1: launch_mfma_inst<D, 3, 1, STREAM, KV8>(grid, persistent, cus, L, a); return true;
+    case 4 * 8 + 1: launch_mfma_inst<D, 4, 1, STREAM, KV8>(grid, persistent, cus, L, a); return true;
     default: return false;
   }
   }
@@ -300,12 +318,12 @@ bool launch_mfma_shape(int nrt, int nw, dim3 grid, bool persistent, int cus, hip
 
 template <int D>
 bool launch_mfma(int nrt, int nw, dim3 grid, bool persistent, bool streaming, bool kv8, int cus,
-                 hipStream_t s, const pa::PartArgs& a) {
+                 const Launch& L, const pa::PartArgs& a) {
   if (kv8)
-    return streaming ? launch_mfma_shape<D, true, true>(nrt, nw, grid, persistent, cus, s, a)
-                     : launch_mfma_shape<D, false, true>(nrt, nw, grid, persistent, cus, s, a);
-  return streaming ? launch_mfma_shape<D, true, false>(nrt, nw, grid, persistent, cus, s, a)
-                   : launch_mfma_shape<D, false, false>(nrt, nw, grid, persistent, cus, s, a);
+    return streaming ? launch_mfma_shape<D, true, true>(nrt, nw, grid, persistent, cus, L, a)
+                     : launch_mfma_shape<D, false, true>(nrt, nw, grid, persistent, cus, L, a);
+  return streaming ? launch_mfma_shape<D, true, false>(nrt, nw, grid, persistent, cus, L, a)
+                   : launch_mfma_shape<D, false, false>(nrt, nw, grid, persistent, cus, L, a);
 }
 
 pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -385,10 +403,8 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
 
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if (o && o->event_begin) {
-    e = hipEventRecord((hipEvent_t)o->event_begin, s);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(begin)");
-  }
+  const Launch L = {s, o ? (hipEvent_t)o->event_begin : nullptr,
+                   o ? (hipEvent_t)o->event_end : nullptr};
   const uint64_t units = (uint64_t)p.num_parts * hkv * d->batch;  // (partition, seq, head)
   const uint64_t nwg = p.row_blocks > 1
                            ? (units + pa::kXcds - 1) / pa::kXcds * pa::kXcds * p.row_blocks
@@ -399,22 +415,18 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
   bool ok = true;
   if (p.path == PA_PATH_MFMA) {
     switch (d->head_dim) {
-      case 64: ok = launch_mfma<64>(nrt, p.waves, grid, p.persistent, p.streaming, kv8, cus, s, a); break;
-      case 128: ok = launch_mfma<128>(nrt, p.waves, grid, p.persistent, p.streaming, kv8, cus, s, a); break;
-      default: ok = launch_mfma<256>(nrt, p.waves, grid, p.persistent, p.streaming, kv8, cus, s, a); break;
+      case 64: ok = launch_mfma<64>(nrt, p.waves, grid, p.persistent, p.streaming, kv8, cus, L, a); break;
+      case 128: ok = launch_mfma<128>(nrt, p.waves, grid, p.persistent, p.streaming, kv8, cus, L, a); break;
+      default: ok = launch_mfma<256>(nrt, p.waves, grid, p.persistent, p.streaming, kv8, cus, L, a); break;
     }
   } else if (d->dtype == PA_F32) {
-    hipLaunchKernelGGL((pa::part_valu<float>), grid, dim3(256), 0, s, a);
+    launch_part(pa::part_valu<float>, grid, dim3(256), L, a);
   } else {
-    hipLaunchKernelGGL((pa::part_valu<uint16_t>), grid, dim3(256), 0, s, a);
+    launch_part(pa::part_valu<uint16_t>, grid, dim3(256), L, a);
   }
   if (!ok) return fail(PA_ERR_UNSUPPORTED, "no kernel for %d row tiles x %d waves", nrt, p.waves);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "partition kernel launch");
-  if (o && o->event_end) {
-    e = hipEventRecord((hipEvent_t)o->event_end, s);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(end)");
-  }
   if (!p.one_shot) {
     pa::ReduceArgs r = {};
     r.out = out;

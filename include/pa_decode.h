@@ -152,9 +152,11 @@ typedef struct pa_options {
                                  unless row blocks re-read K/V), 1 = cached (for callers
                                  whose KV stays in the 256 MB last-level cache from one
                                  call to the next), 2 = non-temporal */
-  void* event_begin;          /* hipEvent_t recorded on the stream just before the
-                                 partition kernel, or NULL */
-  void* event_end;            /* hipEvent_t recorded just after it, or NULL */
+  void* event_begin;          /* hipEvent_t (created, timing enabled) stamped with the
+                                 partition kernel's start, or NULL; with either event
+                                 set the kernel is launched by hipExtLaunchKernel, which
+                                 binds the events to that dispatch */
+  void* event_end;            /* hipEvent_t stamped with the partition kernel's end */
   const float* k_scale;       /* PA_KV_FP8_E4M3: device pointer to the K scale (one float,
                                  4-byte aligned); required then, ignored otherwise */
   const float* v_scale;       /* PA_KV_FP8_E4M3: device pointer to the V scale */

@@ -16,6 +16,8 @@
   of each output row (2^-6 of the row's largest magnitude).
 """
 
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -214,3 +216,26 @@ def test_load_forms_agree_bit_for_bit(sched):
     a = run_gpu(c, schedule=sched, loads=pa.LOADS_CACHED).clone()
     assert torch.equal(run_gpu(c, schedule=sched), a)
     say(f"[loads] schedule={sched}: cached and non-temporal outputs identical")
+
+
+@pytest.mark.parametrize("path,sched", KERNELS)
+def test_timing_events_change_nothing(path, sched):
+    """Timing events bound to the partition kernel's dispatch leave the
+    output bits unchanged, and the interval they carry is positive and lies
+    inside an interval recorded around the whole call."""
+    w = workloads.WORKLOADS["gqa_bf16"]
+    c = workloads.make_case(replace(w, batch=4), device="cuda", window=0)
+    say(f"[case] timing events path={path} sched={sched}")
+    plain = run_gpu(c, path=path, schedule=sched).clone()
+    kb, ke, cb, ce = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+    for e in (kb, ke):
+        e.record()  # torch creates the HIP event on its first record
+    torch.cuda.synchronize()
+    cb.record()
+    timed = run_gpu(c, path=path, schedule=sched, event_begin=kb, event_end=ke)
+    ce.record()
+    torch.cuda.synchronize()
+    assert torch.equal(plain.view(torch.int16), timed.view(torch.int16))
+    kern = kb.elapsed_time(ke)
+    assert 0 < kern <= cb.elapsed_time(ce)
+    assert cb.elapsed_time(kb) >= 0 and ke.elapsed_time(ce) >= 0
