@@ -56,7 +56,7 @@ template <typename T, int VEC, int GP>
 __global__ __launch_bounds__(256) void lse_reduce(ReduceArgs a) {
   typedef float fvec __attribute__((ext_vector_type(VEC)));
   constexpr int UPW = GroupReduce<GP>::UPW;  // units per workgroup
-  constexpr int U = GP == 1 ? 4 : 16;        // partitions in flight per thread per step
+  constexpr int U = GP == 1 ? 4 : 8;         // partitions in flight per thread per step
   const int D = a.head_dim;
   const int D4 = D / VEC;                    // units per row
   __shared__ float lds[4][64];
