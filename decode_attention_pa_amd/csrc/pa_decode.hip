@@ -189,15 +189,16 @@ pa_status make_plan(const pa_dims* d, int32_t window, int32_t hkv, int32_t bs, i
   } else {
     // Enough partitions for ~8 workgroups per CU if every (sequence, KV
     // head) had the longest span (real batches average less), counting
-    // each row block as a workgroup, with partitions of 8..128 chunks:
-    // longer ones amortise each workgroup's set-up and keep the partial
-    // states small, shorter ones would multiply the LSE merge's work.
-    // Constants measured on MI355X.
+    // each row block as a workgroup, with partitions of 8..128 chunks
+    // (4.. at head dim 256: the same K/V bytes per workgroup): longer ones
+    // amortise each workgroup's set-up and keep the partial states small,
+    // shorter ones would multiply the LSE merge's work.  Constants measured
+    // on MI355X.
     const int64_t chunks = cdiv(span_cover, pa::kChunk);
     const int64_t wgs_per_part = std::max<int64_t>(units * r.row_blocks, 1);
     const int64_t want = std::max<int64_t>(1, cdiv(8 * (int64_t)num_cus, wgs_per_part));
     int64_t pc = cdiv(chunks, want);
-    pc = std::max<int64_t>(pc, 8);
+    pc = std::max<int64_t>(pc, d->head_dim == 256 ? 4 : 8);
     pc = std::min<int64_t>(pc, 128);
     r.part_size = (int32_t)(pc * pa::kChunk);
   }
@@ -209,12 +210,27 @@ pa_status make_plan(const pa_dims* d, int32_t window, int32_t hkv, int32_t bs, i
   // faster on a 67 MB cache read from HBM) unless the call re-reads K/V.
   const int loads_req = o ? o->loads : 0;
   if (loads_req < 0 || loads_req > 2) return fail(PA_ERR_INVALID_ARG, "loads %d unknown", loads_req);
-  const bool reread = r.row_blocks > 1;
-  r.streaming = r.path != PA_PATH_MFMA ? 0 : (loads_req == 2 ? 1 : (loads_req == 1 ? 0 : !reread));
   r.num_parts = (int32_t)std::max<int64_t>(1, cdiv(span_cover, r.part_size));
   if (r.num_parts == 1) r.part_size = (int32_t)(cdiv(span_cover, pa::kChunk) * pa::kChunk);
   r.one_shot = r.num_parts == 1;
   if (r.one_shot && sched_req != 2) r.persistent = 0;
+  const int w_req = o ? o->waves : 0;
+  if (r.path == PA_PATH_MFMA && !r.persistent && w_req == 0) {
+    // Grid plans with few waves in flight.  One-shot with under 16 waves
+    // per CU: rows in one-tile blocks of 4 waves (measured on MI355X: 512
+    // sliding-window MTP units of 32 rows, 10 % faster per call as 1024
+    // workgroups x 4 waves than as 512 x 2).  Split at head dim 256: 2 waves
+    // (a long single sequence, 15 % faster than 4).
+    if (r.one_shot && r.row_tiles > 1 && d->head_dim != 256 &&
+        units * r.row_blocks * r.waves < 16 * (int64_t)num_cus) {
+      r.row_tiles = 1;
+      r.waves = 4;
+      r.row_blocks = (r.rows + 15) / 16;
+    }
+    if (!r.one_shot && d->head_dim == 256) r.waves = 2;
+  }
+  const bool reread = r.row_blocks > 1;
+  r.streaming = r.path != PA_PATH_MFMA ? 0 : (loads_req == 2 ? 1 : (loads_req == 1 ? 0 : !reread));
   if (r.one_shot) {
     r.workspace_bytes = 0;
   } else {

@@ -208,8 +208,10 @@ def test_streaming_loads_choice(lib):
     assert pa.plan(dims_of(long, num_blocks=10240), 0, 1, 16)["streaming"] == 1
     assert pa.plan(dims_of(long, num_blocks=10240), 0, 1, 16,
                    loads=pa.LOADS_CACHED)["streaming"] == 0
-    swa = workloads.WORKLOADS["swa_mtp_bf16"]         # 32 rows: two tiles, one block
+    swa = workloads.WORKLOADS["swa_mtp_bf16"]         # one-shot, rows in two blocks
     p = pa.plan(dims_of(swa), 128, 8, 64)
+    assert (p["row_blocks"], p["streaming"]) == (2, 0)
+    p = pa.plan(dims_of(swa), 128, 8, 64, waves=2)    # two tiles, one block
     assert (p["row_blocks"], p["streaming"]) == (1, 1)
     pre = workloads.WORKLOADS["prefill_chunk_bf16"]   # 128 rows: four row blocks share K/V
     p = pa.plan(dims_of(pre), 0, 4, 16)
@@ -290,3 +292,21 @@ def test_binding_rejects_cpu_tensors():
     with pytest.raises(pa.PaError):
         pa.decode(c.new_out(), c.q, c.k_cache, c.v_cache, c.block_tables, c.seq_lens,
                   c.query_lens, c.scale, 0, 1, 16, max_seq_len=50)
+
+
+def test_grid_plans_with_few_waves(lib):
+    # One-shot grid plans under 16 waves per CU split their rows into
+    # one-tile blocks of 4 waves; with enough units, or waves forced, they
+    # keep all rows in one workgroup.
+    swa = workloads.WORKLOADS["swa_mtp_bf16"]        # 512 units x 32 rows, one-shot
+    p = pa.plan(dims_of(swa), 128, 8, 64, num_cus=256)
+    assert (p["one_shot"], p["row_tiles"], p["row_blocks"], p["waves"]) == (1, 1, 2, 4)
+    big = dims_of(swa, batch=1024)                   # 8192 units: plenty of waves
+    p = pa.plan(big, 128, 8, 64, num_cus=256)
+    assert (p["row_tiles"], p["row_blocks"], p["waves"]) == (2, 1, 2)
+    p = pa.plan(dims_of(swa), 128, 8, 64, num_cus=256, waves=2)
+    assert (p["row_tiles"], p["row_blocks"], p["waves"]) == (2, 1, 2)
+    # head dim 256, one long sequence: 4-chunk partitions and 2 waves
+    d256 = workloads.WORKLOADS["d256_decode_bf16"]
+    p = pa.plan(dims_of(d256), 0, 2, 16, num_cus=256)
+    assert (p["part_size"], p["waves"], p["persistent"]) == (128, 2, 0)
