@@ -129,6 +129,35 @@ def ingest_counters(workload: str, window: int, fetch_dir: str, write_dir: str,
     return rec
 
 
+def copy_ceiling(nbytes: int, flush_buf, reps: int = 10) -> dict:
+    """A plain device copy moving the same number of HBM bytes as the
+    partition kernel (half read, half written; capped at 4 GB moved), timed
+    with events around each copy, flushed like the calls when they are: what
+    a trivial kernel reaches at this size on this GPU."""
+    import torch
+    n = max(1, min(nbytes, 4 << 30) // 8)    # float32 elements per buffer
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ts = []
+    for _ in range(reps):
+        if flush_buf is not None:
+            flush_buf.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    ts.sort()
+    moved = 8 * n
+    us = ts[len(ts) // 2]
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"kind": "device copy, read + write", "bytes": moved, "us": round(us, 2),
+            "gbps": round(moved / us / 1e3, 1), "frac": round(moved / us / 1e3 / PEAK_GBPS, 4)}
+
+
 def cpu_baseline(case, out_gpu, budget_s: float, per_call_bytes: int) -> dict:
     """The float64 oracle, as it stands, on a bounded sample of the workload's
     sequences (host cores of this machine), scaled to µs per full call by
@@ -327,6 +356,7 @@ def main(argv=None):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic},
         "host_wall_s": round(wall, 3),
+        "copy_ceiling": copy_ceiling(nb["partition_kernel"], flush_buf),
     }
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(case, out, a.cpu_budget, nb["total"])
