@@ -37,10 +37,9 @@ namespace pa {
 __device__ inline bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
 // 16-byte load of KV data.  STREAM = true marks it non-temporal (streamed past
-// the caches): when the KV a call reads exceeds the last-level cache no line
-// is reused, and on MI355X such loads sustain ~13 % more bandwidth on a
-// block-table gather; below that size the cached form keeps the KV resident
-// in the 256 MB MALL for the next call.
+// the caches): on MI355X such loads sustain ~13 % more bandwidth on a
+// block-table gather.  The cached form serves row blocks that read the same
+// K/V through L2, and callers whose KV stays in the 256 MB MALL between calls.
 template <bool STREAM>
 __device__ inline u32x4 ld_kv(const uint8_t* p) {
   if constexpr (STREAM) return __builtin_nontemporal_load((const u32x4*)p);
