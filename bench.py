@@ -68,10 +68,11 @@ def algorithmic_bytes(case) -> dict:
         kv += w.num_kv_heads * (L - lo) * w.head_dim * 2 * skv
         tables += 4 * ((L - 1) // bs - lo // bs + 1)
     T = sum(case.query_lens_host)
-    qb = T * w.num_q_heads * w.head_dim * s
+    qb = T * w.num_q_heads * w.head_dim * (1 if w.q_dtype == "fp8" else s)   # Q read
+    ob = T * w.num_q_heads * w.head_dim * s                                   # out written
     lens = 8 * w.batch
-    return dict(kv=kv, q=qb, out=qb, tables=tables, lens=lens,
-                total=kv + 2 * qb + tables + lens,
+    return dict(kv=kv, q=qb, out=ob, tables=tables, lens=lens,
+                total=kv + qb + ob + tables + lens,
                 partition_kernel=kv + qb + tables + lens)
 
 
@@ -249,7 +250,7 @@ def main(argv=None):
     w = workloads.WORKLOADS[a.workload]
     window = w.windows[0] if a.window is None else a.window
     case = workloads.make_case(w, device="cuda", window=window)
-    out = torch.empty_like(case.q)
+    out = case.new_out()
     path = {"auto": 0, "valu": pa.PATH_VALU, "mfma": pa.PATH_MFMA}[a.path]
     call = pa.Prepared(out, case.q, case.k_cache, case.v_cache, case.block_tables, case.seq_lens,
                        case.query_lens, case.scale, window, w.num_kv_heads, w.block_size,
@@ -259,7 +260,7 @@ def main(argv=None):
                                  "persistent": pa.SCHED_PERSISTENT}[a.schedule],
                        loads={"auto": 0, "cached": pa.LOADS_CACHED,
                               "streaming": pa.LOADS_STREAMING}[a.loads],
-                       k_scale=case.k_scale, v_scale=case.v_scale)
+                       k_scale=case.k_scale, v_scale=case.v_scale, q_scale=case.q_scale)
     # flush = reading 1 GiB evicts the workload from L2 and the 256 MB MALL
     # with clean lines (a write would leave dirty lines behind to write back)
     flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda") if a.flush else None
@@ -341,13 +342,13 @@ def main(argv=None):
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "dtype": ("fp8 QK, bf16 PV" if w.q_dtype == "fp8" else "bf16") if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {
             "workload": w.name, "description": w.description, "window": window,
             "batch": w.batch, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
             "head_dim": w.head_dim, "block_size": w.block_size, "query_len": w.query_len,
-            "kv_dtype": w.kv_dtype or w.dtype,
+            "kv_dtype": w.kv_dtype or w.dtype, "q_dtype": w.q_dtype or w.dtype,
             "realised_context_tokens": sum(case.seq_lens_host), "plan": call.plan,
             "flush_between_calls": bool(a.flush),
         },

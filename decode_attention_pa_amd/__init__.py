@@ -50,7 +50,7 @@ class Dims(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("max_query_len", ctypes.c_int32),
                 ("max_seq_len", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
                 ("num_blocks", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("kv_format", ctypes.c_int32)]
+                ("kv_format", ctypes.c_int32), ("q_format", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):
@@ -70,7 +70,8 @@ class Options(ctypes.Structure):
                 ("waves", ctypes.c_int32), ("schedule", ctypes.c_int32),
                 ("loads", ctypes.c_int32),
                 ("event_begin", ctypes.c_void_p), ("event_end", ctypes.c_void_p),
-                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("q_scale", ctypes.c_void_p)]
 
 
 _lib = None
@@ -119,13 +120,14 @@ def _check(status: int):
 
 
 KV_NATIVE, KV_FP8_E4M3 = 0, 1
+Q_NATIVE, Q_FP8_E4M3 = 0, 1
 
 
 def make_dims(batch, num_q_heads, head_dim, max_query_len, max_seq_len, max_blocks_per_seq,
-              num_blocks, dtype, kv_format=KV_NATIVE) -> Dims:
+              num_blocks, dtype, kv_format=KV_NATIVE, q_format=Q_NATIVE) -> Dims:
     return Dims(int(batch), int(num_q_heads), int(head_dim), int(max_query_len),
                 int(max_seq_len), int(max_blocks_per_seq), int(num_blocks), int(dtype),
-                int(kv_format))
+                int(kv_format), int(q_format))
 
 
 SCHED_AUTO, SCHED_GRID, SCHED_PERSISTENT = 0, 1, 2
@@ -133,10 +135,10 @@ LOADS_AUTO, LOADS_CACHED, LOADS_STREAMING = 0, 1, 2
 
 
 def make_options(path=0, part_size=0, waves=0, event_begin=None, event_end=None,
-                 schedule=0, loads=0, k_scale=None, v_scale=None) -> Options:
+                 schedule=0, loads=0, k_scale=None, v_scale=None, q_scale=None) -> Options:
     return Options(int(path), int(part_size), int(waves), int(schedule), int(loads),
                    _event_handle(event_begin), _event_handle(event_end),
-                   _scale_ptr(k_scale), _scale_ptr(v_scale))
+                   _scale_ptr(k_scale), _scale_ptr(v_scale), _scale_ptr(q_scale))
 
 
 def _scale_ptr(t):
@@ -146,7 +148,8 @@ def _scale_ptr(t):
     import torch
     if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype != torch.float32 \
             or t.numel() != 1:
-        raise PaError(ERR_INVALID_ARG, "k_scale / v_scale must be float32 CUDA tensors of one element")
+        raise PaError(ERR_INVALID_ARG,
+                      "k_scale / v_scale / q_scale must be float32 CUDA tensors of one element")
     return ctypes.c_void_p(t.data_ptr())
 
 
@@ -195,10 +198,18 @@ def _kv_format(k_cache) -> int:
     return KV_FP8_E4M3 if k_cache.dtype == torch.float8_e4m3fn else KV_NATIVE
 
 
+def _q_format(q) -> int:
+    import torch
+    return Q_FP8_E4M3 if q.dtype == torch.float8_e4m3fn else Q_NATIVE
+
+
 def dims_for(q, k_cache, block_tables, max_query_len, max_seq_len) -> Dims:
+    """Dims of a call; an FP8 query implies a bf16 out (the only one it takes)."""
     T, Hq, D = q.shape
+    qf = _q_format(q)
     return make_dims(block_tables.shape[0], Hq, D, max_query_len, max_seq_len,
-                     block_tables.shape[1], k_cache.shape[0], _dtype_code(q), _kv_format(k_cache))
+                     block_tables.shape[1], k_cache.shape[0],
+                     BF16 if qf == Q_FP8_E4M3 else _dtype_code(q), _kv_format(k_cache), qf)
 
 
 def _validate(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, num_kv_heads, block_size):
@@ -216,9 +227,13 @@ def _validate(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, num_
         if t.dtype != torch.int32:
             raise PaError(ERR_INVALID_ARG, f"{name} must be int32")
     fp8 = k_cache.dtype == torch.float8_e4m3fn
-    if q.dtype != out.dtype:
+    q8 = q.dtype == torch.float8_e4m3fn
+    if q8:
+        if not fp8 or v_cache.dtype != torch.float8_e4m3fn or out.dtype != torch.bfloat16:
+            raise PaError(ERR_INVALID_ARG, "an FP8 q needs FP8 k_cache / v_cache and a bf16 out")
+    elif q.dtype != out.dtype:
         raise PaError(ERR_INVALID_ARG, "q and out must share one dtype")
-    if fp8:
+    elif fp8:
         if v_cache.dtype != torch.float8_e4m3fn or q.dtype != torch.bfloat16:
             raise PaError(ERR_INVALID_ARG, "an FP8 k_cache needs an FP8 v_cache and bf16 q / out")
     elif not (q.dtype == k_cache.dtype == v_cache.dtype):
@@ -247,7 +262,7 @@ def _validate(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, num_
 def decode(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, scale, window,
            num_kv_heads, block_size, max_seq_len, max_query_len=None, workspace=None,
            stream=None, path=0, part_size=0, waves=0, event_begin=None, event_end=None,
-           schedule=0, loads=0, k_scale=None, v_scale=None):
+           schedule=0, loads=0, k_scale=None, v_scale=None, q_scale=None):
     """Runs pa_decode_ex on torch tensors; returns ``out``.
 
     ``max_seq_len`` / ``max_query_len`` are host-known upper bounds of the
@@ -262,7 +277,7 @@ def decode(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, scale, 
         max_query_len = max(1, min(max_query_len, int(max_seq_len)))
     dims = dims_for(q, k_cache, block_tables, max_query_len, max_seq_len)
     opts = make_options(path, part_size, waves, event_begin, event_end, schedule, loads,
-                        k_scale, v_scale)
+                        k_scale, v_scale, q_scale)
     need = workspace_size(dims, window, num_kv_heads, block_size, path=path,
                           part_size=part_size, waves=waves, schedule=schedule)
     if workspace is None and need:
@@ -311,13 +326,13 @@ class Prepared:
     def __init__(self, out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, scale, window,
                  num_kv_heads, block_size, max_seq_len, max_query_len, workspace=None,
                  stream=None, path=0, part_size=0, waves=0, event_begin=None, event_end=None,
-                 schedule=0, loads=0, k_scale=None, v_scale=None):
+                 schedule=0, loads=0, k_scale=None, v_scale=None, q_scale=None):
         import torch
         _validate(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, num_kv_heads,
                   block_size)
         self.dims = dims_for(q, k_cache, block_tables, max_query_len, max_seq_len)
         self.opts = make_options(path, part_size, waves, event_begin, event_end, schedule, loads,
-                                 k_scale, v_scale)
+                                 k_scale, v_scale, q_scale)
         self._events = (event_begin, event_end)
         self.plan = plan(self.dims, window, num_kv_heads, block_size,
                          num_cus=torch.cuda.get_device_properties(q.device).multi_processor_count,
@@ -328,7 +343,8 @@ class Prepared:
         if workspace is None and need:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         self.workspace = workspace
-        self._keep = (out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, k_scale, v_scale)
+        self._keep = (out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, k_scale, v_scale,
+                      q_scale)
         vp = ctypes.c_void_p
         self.args = (
             vp(out.data_ptr()), vp(q.data_ptr()), vp(k_cache.data_ptr()), vp(v_cache.data_ptr()),

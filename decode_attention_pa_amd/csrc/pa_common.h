@@ -129,6 +129,7 @@ struct PartArgs {
   int head_dim;                // D (the vector kernel reads it at run time)
   const float* k_scale;        // FP8 KV: device scalars, K = code * k_scale, V = code * v_scale
   const float* v_scale;        // (null for native caches)
+  const float* q_scale;        // FP8 Q: device scalar, Q = code * q_scale (else null)
 };
 
 // Work-item of a partition workgroup.  The grid is 1-D and ordered with the

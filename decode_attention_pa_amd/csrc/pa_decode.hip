@@ -75,6 +75,10 @@ pa_status check_shape(const pa_dims* d, int32_t window, int32_t num_kv_heads, in
     return fail(PA_ERR_UNSUPPORTED, "head_dim %d outside [1, %d]", d->head_dim, pa::kValuMaxD);
   if (d->kv_format == PA_KV_FP8_E4M3 && !mfma_head_dim(d->head_dim))
     return fail(PA_ERR_UNSUPPORTED, "an FP8 KV cache needs head_dim 64, 128 or 256");
+  if (d->q_format != PA_Q_NATIVE && d->q_format != PA_Q_FP8_E4M3)
+    return fail(PA_ERR_INVALID_ARG, "q_format %d unknown", d->q_format);
+  if (d->q_format == PA_Q_FP8_E4M3 && d->kv_format != PA_KV_FP8_E4M3)
+    return fail(PA_ERR_UNSUPPORTED, "an FP8 query needs an FP8 KV cache");
   if (num_kv_heads < 1 || num_kv_heads > 65535)
     return fail(PA_ERR_INVALID_ARG, "num_kv_heads %d outside [1, 65535]", num_kv_heads);
   if (d->num_q_heads < 1 || d->num_q_heads % num_kv_heads)
@@ -297,49 +301,52 @@ void launch_part(K kernel, dim3 grid, dim3 block, const Launch& L, const pa::Par
     hipLaunchKernelGGL(kernel, grid, block, 0, L.s, a);
 }
 
-template <int D, int NRT, int NW, bool STREAM, bool KV8>
+template <int D, int NRT, int NW, bool STREAM, bool KV8, bool Q8>
 void launch_mfma_inst(dim3 grid, bool persistent, int cus, const Launch& L, const pa::PartArgs& a) {
   if (persistent) {
-    const void* fn = (const void*)pa::part_mfma_ps<D, NRT, NW, STREAM, KV8>;
+    const void* fn = (const void*)pa::part_mfma_ps<D, NRT, NW, STREAM, KV8, Q8>;
     const dim3 pgrid(resident_wgs(fn, 64 * NW, cus));
-    launch_part(pa::part_mfma_ps<D, NRT, NW, STREAM, KV8>, pgrid, dim3(64 * NW), L, a);
+    launch_part(pa::part_mfma_ps<D, NRT, NW, STREAM, KV8, Q8>, pgrid, dim3(64 * NW), L, a);
   } else {
-    launch_part(pa::part_mfma<D, NRT, NW, STREAM, KV8>, grid, dim3(64 * NW), L, a);
+    launch_part(pa::part_mfma<D, NRT, NW, STREAM, KV8, Q8>, grid, dim3(64 * NW), L, a);
   }
 }
 
-template <int D, bool STREAM, bool KV8>
+template <int D, bool STREAM, bool KV8, bool Q8>
 bool launch_mfma_shape(int nrt, int nw, dim3 grid, bool persistent, int cus, const Launch& L,
                        const pa::PartArgs& a) {
   if constexpr (D == 256) {  // one row tile (the plan never asks for more)
     switch (nrt * 8 + nw) {
-      case 1 * 8 + 1: launch_mfma_inst<D, 1, 1, STREAM, KV8>(grid, persistent, cus, L, a); return true;
-      case 1 * 8 + 2: launch_mfma_inst<D, 1, 2, STREAM, KV8>(grid, persistent, cus, L, a); return true;
-      case 1 * 8 + 4: launch_mfma_inst<D, 1, 4, STREAM, KV8>(grid, persistent, cus, L, a); return true;
+      case 1 * 8 + 1: launch_mfma_inst<D, 1, 1, STREAM, KV8, Q8>(grid, persistent, cus, L, a); return true;
+      case 1 * 8 + 2: launch_mfma_inst<D, 1, 2, STREAM, KV8, Q8>(grid, persistent, cus, L, a); return true;
+      case 1 * 8 + 4: launch_mfma_inst<D, 1, 4, STREAM, KV8, Q8>(grid, persistent, cus, L, a); return true;
       default: return false;
     }
   } else {
   switch (nrt * 8 + nw) {
-    case 1 * 8 + 1: launch_mfma_inst<D, 1, 1, STREAM, KV8>(grid, persistent, cus, L, a); return true;
-    case 1 * 8 + 2: launch_mfma_inst<D, 1, 2, STREAM, KV8>(grid, persistent, cus, L, a); return true;
-    case 1 * 8 + 4: launch_mfma_inst<D, 1, 4, STREAM, KV8>(grid, persistent, cus, L, a); return true;
-    case 2 * 8 + 1: launch_mfma_inst<D, 2, 1, STREAM, KV8>(grid, persistent, cus, L, a); return true;
-    case 2 * 8 + 2: launch_mfma_inst<D, 2, 2, STREAM, KV8>(grid, persistent, cus, L, a); return true;
-    case 3 * 8 + 1: launch_mfma_inst<D, 3, 1, STREAM, KV8>(grid, persistent, cus, L, a); return true;
-    case 4 * 8 + 1: launch_mfma_inst<D, 4, 1, STREAM, KV8>(grid, persistent, cus, L, a); return true;
+    case 1 * 8 + 1: launch_mfma_inst<D, 1, 1, STREAM, KV8, Q8>(grid, persistent, cus, L, a); return true;
+    case 1 * 8 + 2: launch_mfma_inst<D, 1, 2, STREAM, KV8, Q8>(grid, persistent, cus, L, a); return true;
+    case 1 * 8 + 4: launch_mfma_inst<D, 1, 4, STREAM, KV8, Q8>(grid, persistent, cus, L, a); return true;
+    case 2 * 8 + 1: launch_mfma_inst<D, 2, 1, STREAM, KV8, Q8>(grid, persistent, cus, L, a); return true;
+    case 2 * 8 + 2: launch_mfma_inst<D, 2, 2, STREAM, KV8, Q8>(grid, persistent, cus, L, a); return true;
+    case 3 * 8 + 1: launch_mfma_inst<D, 3, 1, STREAM, KV8, Q8>(grid, persistent, cus, L, a); return true;
+    case 4 * 8 + 1: launch_mfma_inst<D, 4, 1, STREAM, KV8, Q8>(grid, persistent, cus, L, a); return true;
     default: return false;
   }
   }
 }
 
 template <int D>
-bool launch_mfma(int nrt, int nw, dim3 grid, bool persistent, bool streaming, bool kv8, int cus,
-                 const Launch& L, const pa::PartArgs& a) {
+bool launch_mfma(int nrt, int nw, dim3 grid, bool persistent, bool streaming, bool kv8, bool q8,
+                 int cus, const Launch& L, const pa::PartArgs& a) {
+  if (q8)
+    return streaming ? launch_mfma_shape<D, true, true, true>(nrt, nw, grid, persistent, cus, L, a)
+                     : launch_mfma_shape<D, false, true, true>(nrt, nw, grid, persistent, cus, L, a);
   if (kv8)
-    return streaming ? launch_mfma_shape<D, true, true>(nrt, nw, grid, persistent, cus, L, a)
-                     : launch_mfma_shape<D, false, true>(nrt, nw, grid, persistent, cus, L, a);
-  return streaming ? launch_mfma_shape<D, true, false>(nrt, nw, grid, persistent, cus, L, a)
-                   : launch_mfma_shape<D, false, false>(nrt, nw, grid, persistent, cus, L, a);
+    return streaming ? launch_mfma_shape<D, true, true, false>(nrt, nw, grid, persistent, cus, L, a)
+                     : launch_mfma_shape<D, false, true, false>(nrt, nw, grid, persistent, cus, L, a);
+  return streaming ? launch_mfma_shape<D, true, false, false>(nrt, nw, grid, persistent, cus, L, a)
+                   : launch_mfma_shape<D, false, false, false>(nrt, nw, grid, persistent, cus, L, a);
 }
 
 pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -366,6 +373,14 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
                   "an FP8 KV cache needs k_scale and v_scale (pa_decode_ex, pa_options)");
     if (!aligned(o->k_scale, 4) || !aligned(o->v_scale, 4))
       return fail(PA_ERR_INVALID_ARG, "k_scale and v_scale must be 4-byte aligned");
+  }
+  const bool q8 = d->q_format == PA_Q_FP8_E4M3;
+  if (q8) {
+    // aiter PR #2914 review: an FP8 query without its scale must be refused
+    if (!o || !o->q_scale)
+      return fail(PA_ERR_INVALID_ARG, "an FP8 query needs q_scale (pa_decode_ex, pa_options)");
+    if (!aligned(o->q_scale, 4))
+      return fail(PA_ERR_INVALID_ARG, "q_scale must be 4-byte aligned");
   }
   if (d->batch == 0) return PA_OK;
   int cus = 0;
@@ -414,6 +429,7 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
   a.batch = d->batch;
   a.k_scale = kv8 ? o->k_scale : nullptr;
   a.v_scale = kv8 ? o->v_scale : nullptr;
+  a.q_scale = q8 ? o->q_scale : nullptr;
   a.row_blocks = p.row_blocks;
   a.head_dim = d->head_dim;
 
@@ -431,9 +447,9 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
   bool ok = true;
   if (p.path == PA_PATH_MFMA) {
     switch (d->head_dim) {
-      case 64: ok = launch_mfma<64>(nrt, p.waves, grid, p.persistent, p.streaming, kv8, cus, L, a); break;
-      case 128: ok = launch_mfma<128>(nrt, p.waves, grid, p.persistent, p.streaming, kv8, cus, L, a); break;
-      default: ok = launch_mfma<256>(nrt, p.waves, grid, p.persistent, p.streaming, kv8, cus, L, a); break;
+      case 64: ok = launch_mfma<64>(nrt, p.waves, grid, p.persistent, p.streaming, kv8, q8, cus, L, a); break;
+      case 128: ok = launch_mfma<128>(nrt, p.waves, grid, p.persistent, p.streaming, kv8, q8, cus, L, a); break;
+      default: ok = launch_mfma<256>(nrt, p.waves, grid, p.persistent, p.streaming, kv8, q8, cus, L, a); break;
     }
   } else if (d->dtype == PA_F32) {
     launch_part(pa::part_valu<float>, grid, dim3(256), L, a);

@@ -30,6 +30,8 @@
 // max, exp-sum and normalised partial output for the LSE reduce.
 #pragma once
 
+#include <type_traits>
+
 #include "pa_common.h"
 
 namespace pa {
@@ -93,7 +95,7 @@ struct ChunkBlocks {
 // 16 * (4c + lg) + 8x .. +7, and Q^T is loaded in the same order (a
 // contraction may visit its index in any order, as long as both operands
 // agree).
-template <int D, int NRT, int NW, bool STREAM, bool KV8>
+template <int D, int NRT, int NW, bool STREAM, bool KV8, bool Q8>
 __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L, int q, int qoff,
                                          const SeqView& sv, int j_first, int j_last, int slot,
                                          bool write_out, int r0 = 0) {
@@ -126,9 +128,13 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
   const size_t blk_stride = slab * (size_t)a.num_kv_heads;
   const size_t head_off = slab * (size_t)h;
 
+  static_assert(!Q8 || KV8, "an FP8 query goes with an FP8 KV cache");
+  // Q^T operand of one k-step: 8 bf16 values, or 8 E4M3 codes (FP8 query).
+  using QOp = std::conditional_t<Q8, uint64_t, bf16x8>;
+
   // Per-row visible interval inside this partition, and Q^T operands.
   int tlo[NRT], thi[NRT];
-  bf16x8 qf[NRT][KS];
+  QOp qf[NRT][KS];
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
     const int n = r0 + rt * 16 + ln;
@@ -141,18 +147,25 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
         tlo[rt] = 0x7fffffff;
         thi[rt] = -1;
       }
-      const uint16_t* qp =
-          (const uint16_t*)a.q + ((size_t)(qoff + i) * a.num_q_heads + (size_t)h * G + g) * D;
+      const size_t qrow = ((size_t)(qoff + i) * a.num_q_heads + (size_t)h * G + g) * D;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const int d0 = KV8 ? 16 * (4 * (s >> 1) + lg) + 8 * (s & 1) : 8 * (4 * s + lg);
-        qf[rt][s] = as_bf16x8(*(const u32x4*)(qp + d0));
+        if constexpr (Q8)  // 8 codes = 8 bytes at dim d0 of the row
+          qf[rt][s] = *(const uint64_t*)((const uint8_t*)a.q + qrow + d0);
+        else
+          qf[rt][s] = as_bf16x8(*(const u32x4*)((const uint16_t*)a.q + qrow + d0));
       }
     } else {
       tlo[rt] = 0x7fffffff;
       thi[rt] = -1;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) qf[rt][s] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+      for (int s = 0; s < KS; ++s) {
+        if constexpr (Q8)
+          qf[rt][s] = 0;
+        else
+          qf[rt][s] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+      }
     }
   }
 
@@ -213,6 +226,11 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
       for (int dt = 0; dt < DT; ++dt) vr[dt] = ld_kv<STREAM>(vp + (dummy ? 0 : 256 * dt));
     }
   };
+  // FP8 A operand of k-step s of tile t: its 8 E4M3 codes as they were loaded
+  auto k_codes = [&](const u32x4 (&kr)[2][KL], int t, int s) -> uint64_t {
+    const u32x4& w = kr[t][s >> 1];
+    return (s & 1) ? ((uint64_t)w[3] << 32 | w[2]) : ((uint64_t)w[1] << 32 | w[0]);
+  };
   // bf16 A operand of k-step s of tile t
   auto k_operand = [&](const u32x4 (&kr)[2][KL], int t, int s) -> bf16x8 {
     if constexpr (KV8) {
@@ -238,6 +256,7 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
     scale_log2 *= *a.k_scale;
     v_scale = *a.v_scale;
   }
+  if constexpr (Q8) scale_log2 *= *a.q_scale;
 
   // Software pipeline, one chunk deep: the next chunk's K rows are requested
   // as soon as QK has consumed the current ones, its V columns as soon as PV
@@ -264,8 +283,15 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
       f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(kr, 0, s), qf[rt][s], sa, 0, 0, 0);
-        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(kr, 1, s), qf[rt][s], sb, 0, 0, 0);
+        if constexpr (Q8) {  // E4M3 x E4M3 products, fp32 accumulation
+          sa = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k_codes(kr, 0, s), (long)qf[rt][s], sa,
+                                                         0, 0, 0);
+          sb = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k_codes(kr, 1, s), (long)qf[rt][s], sb,
+                                                         0, 0, 0);
+        } else {
+          sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(kr, 0, s), qf[rt][s], sa, 0, 0, 0);
+          sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(kr, 1, s), qf[rt][s], sb, 0, 0, 0);
+        }
       }
       // visible iff tlo <= t <= thi, as one unsigned comparison (rows that
       // see nothing have tlo = 2^31 - 1, thi = -1: no t >= 0 passes)
@@ -427,7 +453,7 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
 }
 
 // Grid schedule: one workgroup per (partition, sequence, KV head).
-template <int D, int NRT, int NW, bool STREAM, bool KV8>
+template <int D, int NRT, int NW, bool STREAM, bool KV8, bool Q8>
 __global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
   const PartItem it = part_item(a);
   const int L = a.seq_lens[it.b];
@@ -437,7 +463,7 @@ __global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
   const int r0 = it.rb * 16 * NRT;                // first packed row of this block
   if (r0 >= a.group * q) return;                 // no row of this sequence is in it
   const int qoff = wave_row_offset(a.query_lens, it.b);
-  mfma_run<D, NRT, NW, STREAM, KV8>(a, it.b, it.h, L, q, qoff, sv, it.j, it.j, it.j, sv.nparts == 1,
+  mfma_run<D, NRT, NW, STREAM, KV8, Q8>(a, it.b, it.h, L, q, qoff, sv, it.j, it.j, it.j, sv.nparts == 1,
                                     r0);
 }
 
@@ -451,7 +477,7 @@ __global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
 // whole unit writes `out`; otherwise it stores its state in slot k = its
 // ordinal among the unit's runs, and the unit's last run records the number
 // of states for the merge (0 when the unit was written directly).
-template <int D, int NRT, int NW, bool STREAM, bool KV8>
+template <int D, int NRT, int NW, bool STREAM, bool KV8, bool Q8>
 __global__ __launch_bounds__(64 * NW) void part_mfma_ps(PartArgs a) {
   constexpr int NT = 64 * NW;
   __shared__ int s_np[kPsMaxBatch + 1];  // exclusive prefix of partitions per sequence
@@ -532,7 +558,7 @@ __global__ __launch_bounds__(64 * NW) void part_mfma_ps(PartArgs a) {
     const long w_first = ((A + 1) * W + total - 1) / total - 1;
     const int slot = (int)((long)blockIdx.x - w_first);
     const bool whole = (j1 == 0 && j2 == np_b - 1);
-    mfma_run<D, NRT, NW, STREAM, KV8>(a, b, h, L, q, s_q[b], sv, j1, j2, slot, whole);
+    mfma_run<D, NRT, NW, STREAM, KV8, Q8>(a, b, h, L, q, s_q[b], sv, j1, j2, slot, whole);
     // (one-shot plans have no workspace: every unit is whole and no merge runs)
     if (j2 == np_b - 1 && tid == 0 && a.ws_runs != nullptr)
       a.ws_runs[(size_t)b * H + h] = whole ? 0 : slot + 1;

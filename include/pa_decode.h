@@ -47,7 +47,8 @@
  *                 slot t % block_size
  *   seq_lens, query_lens   int32 [B]
  * q and out share one element type (pa_dims.dtype); k_cache and v_cache share
- * it too, or hold FP8 codes (pa_dims.kv_format).
+ * it too, or hold FP8 codes (pa_dims.kv_format); over an FP8 cache q may hold
+ * FP8 codes as well (pa_dims.q_format, [T, H_q, D] bytes).
  *
  * Device-side preconditions (not checked on the hot path; violating them is
  * undefined behaviour):  0 <= q_b <= L_b <= max_seq_len, q_b <= max_query_len,
@@ -100,6 +101,18 @@ typedef enum pa_kv_format {
                                rejected (PA_ERR_INVALID_ARG) */
 } pa_kv_format;
 
+/* Element format of q. */
+typedef enum pa_q_format {
+  PA_Q_NATIVE = 0,          /* q in pa_dims.dtype */
+  PA_Q_FP8_E4M3 = 1         /* OCP E4M3 codes (one byte) with a per-tensor scale: value =
+                               code * (*q_scale); out stays bf16.  Needs an FP8 KV cache
+                               (QK^T then runs on the FP8 matrix cores) and the
+                               matrix-core path.  aiter PR #2914 (review of
+                               pa_decode_gluon): an FP8 query must come with its query
+                               scale, and a call without it is rejected
+                               (PA_ERR_INVALID_ARG) */
+} pa_q_format;
+
 /* Shapes a raw-pointer interface cannot infer.  All host-side values. */
 typedef struct pa_dims {
   int32_t batch;              /* B >= 0 */
@@ -110,8 +123,9 @@ typedef struct pa_dims {
   int32_t max_seq_len;        /* upper bound on seq_lens[b], >= 1 */
   int32_t max_blocks_per_seq; /* row stride of block_tables, >= ceil(max_seq_len/block_size) */
   int32_t num_blocks;         /* physical blocks in each cache, >= 1 */
-  int32_t dtype;              /* pa_dtype of q and out (and of k_cache, v_cache when native) */
+  int32_t dtype;              /* pa_dtype of out (and of q, k_cache, v_cache when native) */
   int32_t kv_format;          /* pa_kv_format of k_cache and v_cache */
+  int32_t q_format;           /* pa_q_format of q */
 } pa_dims;
 
 /* Kernel families for the partition step. */
@@ -160,6 +174,8 @@ typedef struct pa_options {
   const float* k_scale;       /* PA_KV_FP8_E4M3: device pointer to the K scale (one float,
                                  4-byte aligned); required then, ignored otherwise */
   const float* v_scale;       /* PA_KV_FP8_E4M3: device pointer to the V scale */
+  const float* q_scale;       /* PA_Q_FP8_E4M3: device pointer to the Q scale (one float,
+                                 4-byte aligned); required then, ignored otherwise */
 } pa_options;
 
 /*

@@ -28,6 +28,8 @@ def run_gpu(case, out=None, **opts):
     if case.k_scale is not None:
         opts.setdefault("k_scale", case.k_scale)
         opts.setdefault("v_scale", case.v_scale)
+    if case.q_scale is not None:
+        opts.setdefault("q_scale", case.q_scale)
     pa.decode(out, case.q, case.k_cache, case.v_cache, case.block_tables, case.seq_lens,
               case.query_lens, case.scale, case.window, case.w.num_kv_heads, case.w.block_size,
               max_seq_len=case.w.max_seq_len, max_query_len=max(case.w.query_len,
@@ -64,7 +66,8 @@ def oracle_inputs(case, seqs=None):
         for kk, p in enumerate(sp[b]["blocks"]):
             ctab[r, kk] = remap[int(p)] if p >= 0 else 0
         rows.extend(range(sp[b]["qoff"], sp[b]["qoff"] + case.query_lens_host[b]))
-    qh = case.q.float().cpu().numpy()[rows] if rows else np.zeros((0,) + tuple(case.q.shape[1:]))
+    qh = _host_values(case.q, case.w.q_scale)[rows] if rows else \
+        np.zeros((0,) + tuple(case.q.shape[1:]))
     return dict(q=qh, k_cache=k, v_cache=v, block_tables=ctab,
                 seq_lens=np.array([case.seq_lens_host[b] for b in seqs]),
                 query_lens=np.array([case.query_lens_host[b] for b in seqs]),
@@ -73,7 +76,8 @@ def oracle_inputs(case, seqs=None):
 
 
 def _host_values(t, scale):
-    """Cache blocks as host values: FP8 codes dequantized by the oracle."""
+    """Device values on the host: FP8 codes (caches, queries) dequantized by
+    the oracle."""
     if t.dtype == torch.float8_e4m3fn:
         return ref.dequantize(t.view(torch.uint8).cpu().numpy(), scale)
     return t.float().cpu().numpy()

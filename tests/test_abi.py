@@ -54,7 +54,8 @@ def dims_of(w: workloads.Workload, max_query_len=None, **over):
              max_query_len=w.query_len if max_query_len is None else max_query_len, max_seq_len=w.max_seq_len,
              max_blocks_per_seq=w.max_blocks_per_seq, num_blocks=1000,
              dtype=pa.F32 if w.dtype == "f32" else pa.BF16,
-             kv_format=pa.KV_FP8_E4M3 if w.kv_dtype == "fp8" else pa.KV_NATIVE)
+             kv_format=pa.KV_FP8_E4M3 if w.kv_dtype == "fp8" else pa.KV_NATIVE,
+             q_format=pa.Q_FP8_E4M3 if w.q_dtype == "fp8" else pa.Q_NATIVE)
     d.update(over)
     return pa.make_dims(**d)
 
@@ -310,3 +311,22 @@ def test_grid_plans_with_few_waves(lib):
     d256 = workloads.WORKLOADS["d256_decode_bf16"]
     p = pa.plan(dims_of(d256), 0, 2, 16, num_cus=256)
     assert (p["part_size"], p["waves"], p["persistent"]) == (128, 2, 0)
+
+
+def test_fp8_query_format_rules(lib):
+    w = workloads.WORKLOADS["gqa_fp8qkv"]
+    d = dims_of(w, kv_format=pa.KV_FP8_E4M3, q_format=pa.Q_FP8_E4M3)
+    p = pa.plan(d, 0, 8, 16)
+    assert p["path"] == pa.PATH_MFMA and p["persistent"] == 1
+    # the same plan as bf16 queries over the same cache
+    assert p == pa.plan(dims_of(w, kv_format=pa.KV_FP8_E4M3, q_format=pa.Q_NATIVE), 0, 8, 16)
+    for over, kw, code in [(dict(q_format=2), {}, pa.ERR_INVALID_ARG),
+                           (dict(kv_format=pa.KV_NATIVE, q_format=pa.Q_FP8_E4M3), {},
+                            pa.ERR_UNSUPPORTED),
+                           (dict(kv_format=pa.KV_FP8_E4M3, q_format=pa.Q_FP8_E4M3),
+                            dict(path=pa.PATH_VALU), pa.ERR_UNSUPPORTED),
+                           (dict(kv_format=pa.KV_FP8_E4M3, q_format=pa.Q_FP8_E4M3, head_dim=96),
+                            {}, pa.ERR_UNSUPPORTED)]:
+        with pytest.raises(pa.PaError) as e:
+            pa.plan(dims_of(w, **over), 0, 8, 16, **kw)
+        assert e.value.status == code, over

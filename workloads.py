@@ -19,6 +19,8 @@ Layouts (the library's contract):
                   [num_blocks, H_kv, bs/16, 2, D/16, 8, 16], v_cache
                   [num_blocks, H_kv, bs/16, D, 16]; value = code * k_scale
                   (v_scale), per-tensor float32 scales on the device
+    FP8 queries (q_dtype "fp8"): q holds the E4M3 codes of the same N(0, 1)
+                  draws (nearest code of x / q_scale); out stays bf16
     block_tables  int32 [B, max_blocks_per_seq]
     seq_lens      int32 [B]  (context length, query tokens included)
     query_lens    int32 [B]
@@ -68,6 +70,8 @@ class Workload:
     kv_dtype: str = ""         # "" = the workload dtype, "fp8" = OCP E4M3 codes + scales
     k_scale: float = 0.0123    # FP8 only: K value = code * k_scale
     v_scale: float = 0.0157    # FP8 only: V value = code * v_scale
+    q_dtype: str = ""          # "" = the workload dtype, "fp8" = OCP E4M3 codes + q_scale
+    q_scale: float = 0.0371    # FP8 query only: Q value = code * q_scale
 
 
 WORKLOADS = {
@@ -104,6 +108,14 @@ WORKLOADS = {
         max_seq_len=8192, len_range=(512, 8192),
         description="GQA decode, bf16 queries over an FP8 (E4M3) KV cache with "
                     "per-tensor scales: B=32, 32/8 heads, D=128, bs=16, "
+                    "context U[512, 8192], q_len 1, window 0"),
+    "gqa_fp8qkv": Workload(
+        name="gqa_fp8qkv", dtype="bf16", kv_dtype="fp8", q_dtype="fp8", batch=32,
+        num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, query_len=1,
+        windows=(0,), scale=1.0 / math.sqrt(128.0), seed=2, max_blocks_per_seq=512,
+        max_seq_len=8192, len_range=(512, 8192),
+        description="GQA decode, FP8 (E4M3) queries over an FP8 KV cache with "
+                    "per-tensor scales, bf16 out: B=32, 32/8 heads, D=128, bs=16, "
                     "context U[512, 8192], q_len 1, window 0"),
     "d256_decode_bf16": Workload(
         name="d256_decode_bf16", dtype="bf16", batch=1, num_q_heads=16, num_kv_heads=2,
@@ -187,6 +199,7 @@ class Case:
     extra: dict = field(default_factory=dict)
     k_scale: torch.Tensor | None = None   # FP8 caches: float32 [1] on the device
     v_scale: torch.Tensor | None = None
+    q_scale: torch.Tensor | None = None   # FP8 queries: float32 [1] on the device
 
     @property
     def scale(self) -> float:
@@ -197,7 +210,7 @@ class Case:
         return int(self.k_cache.shape[0])
 
     def new_out(self) -> torch.Tensor:
-        return torch.empty_like(self.q)
+        return torch.empty(self.q.shape, dtype=torch_dtype(self.w.dtype), device=self.q.device)
 
 
 def _lengths(w: Workload, g: torch.Generator) -> tuple[list, list]:
@@ -263,6 +276,8 @@ def make_case(w: Workload | str, device="cpu", window: int | None = None,
     _fill_normal(q, vg)
     if q_gain != 1.0:
         q.copy_((q.float() * q_gain).to(dt))
+    if w.q_dtype == "fp8":
+        q = to_e4m3(q, w.q_scale)
     D = w.head_dim
     fp8 = w.kv_dtype == "fp8"
     E = 16 if fp8 else 8                    # elements per 16-byte column / V group
@@ -314,7 +329,9 @@ def make_case(w: Workload | str, device="cpu", window: int | None = None,
         seq_lens_host=lens, query_lens_host=qls, tables_host=tables,
         used_blocks=used, unused_blocks=unused,
         k_scale=torch.tensor([w.k_scale], dtype=torch.float32, device=dev) if fp8 else None,
-        v_scale=torch.tensor([w.v_scale], dtype=torch.float32, device=dev) if fp8 else None)
+        v_scale=torch.tensor([w.v_scale], dtype=torch.float32, device=dev) if fp8 else None,
+        q_scale=torch.tensor([w.q_scale], dtype=torch.float32, device=dev)
+        if w.q_dtype == "fp8" else None)
 
 
 def custom(name="custom", **kw) -> Workload:
