@@ -7,10 +7,11 @@
  * PagedAttention" (#116), "What changes — Interface":
  *     PagedAttention(dst, q, kCache, vCache, blockTables, seqLens,
  *                    queryLens, scale, window)
- * with its window rule (summary): for window > 0 the token at position p
- * attends to positions p-window+1 .. p; window == 0 is unlimited causal
- * attention.  Query heads are grouped onto KV heads by H_q / H_kv (executorch
- * PR #18759, review of sdpa_decode_splitk: native GQA via H_q // H_kv).
+ * with its window rule (summary): a positive window w limits the query at
+ * position p to the w positions ending at p (p-w+1 to p); w = 0 leaves
+ * causal attention unlimited.  Query heads map onto KV heads by integer
+ * division by the group size H_q / H_kv (executorch PR #18759, review of
+ * sdpa_decode_splitk: native grouped-query attention).
  * Multi-token queries (aiter PR #2914 "Pa gluon swa mtp opt": sliding-window
  * MTP decode) are the trailing query_lens[b] positions of the context and
  * are causal among themselves.  Long contexts are cut into partitions whose

@@ -2,12 +2,12 @@
 
 Pure-Python loops, Python floats (IEEE double).  Deliberately written without
 the range arithmetic of ``paged_attention``: it walks every position of the
-context and tests visibility per position with the page's wording — gllm
-"feat(backend): sliding-window PagedAttention" (#116), summary: with window
-> 0 the token at position p attends to positions p-window+1 through p,
-window == 0 is unlimited causal — i.e. t is visible iff t <= p and, when a
-window is set, fewer than ``window`` positions separate t from p.  Only for
-tiny inputs.
+context and tests visibility per position with the page's rule — gllm
+"feat(backend): sliding-window PagedAttention" (#116), summary: a positive
+window limits the query at position p to the last ``window`` positions up to
+and including p, and a zero window leaves causal attention unlimited — i.e.
+t is visible iff t <= p and, when a window is set, fewer than ``window``
+positions separate t from p.  Only for tiny inputs.
 """
 
 from __future__ import annotations

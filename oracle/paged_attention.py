@@ -61,9 +61,9 @@ def row_position(seq_len: int, query_len: int, i: int) -> int:
     """Absolute position of query token ``i`` of a sequence.
 
     Reading: the query tokens are the last ``query_len`` positions of the
-    ``seq_len``-position context (gllm #116 "Verification": a 5-token chunk
-    "over a 300-token context"; aiter PR #2914: MTP decode), so their keys and
-    values are already in the cache.
+    ``seq_len``-position context (gllm #116 "Verification": its GPU test puts
+    5 query tokens at the end of a context of 300 positions; aiter PR #2914:
+    MTP decode), so their keys and values are already in the cache.
     """
     return seq_len - query_len + i
 
@@ -71,10 +71,11 @@ def row_position(seq_len: int, query_len: int, i: int) -> int:
 def visible_range(seq_len: int, query_len: int, i: int, window: int) -> tuple[int, int]:
     """Inclusive range [lo, p] of positions query token ``i`` attends to.
 
-    gllm #116, summary: with window > 0 the token at position p attends only
-    to p - window + 1 .. p; window == 0 is unlimited causal attention.
-    "What changes — CPU reference": the range starts at max(0, end - window)
-    where end = p + 1.
+    gllm #116, summary: a positive window restricts the query at position p
+    to the ``window`` positions ending at p itself; a zero window keeps causal
+    attention unlimited.
+    "What changes — CPU reference": its lower end is max(0, end - window)
+    with end = p + 1.
     """
     p = row_position(seq_len, query_len, i)
     lo = 0 if window == 0 else max(0, p + 1 - window)

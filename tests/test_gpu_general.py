@@ -2,10 +2,11 @@
 blocks), head dim 256 (matrix cores) and head dims off the 8-dim grid (the
 vector kernel, K one row per slot), against the float64 oracle.
 
-The mixed batch is the GPU test shape of gllm "feat(backend): sliding-window
-PagedAttention" (#116), "Verification": a 5-token prefill chunk over a
-300-token context plus a decode row over 40, windows 16, 100 and 4096, head
-dims 64 and 66.  Values are synthetic (seeded N(0, 1)); the pages print none.
+The mixed batch follows the GPU test of gllm "feat(backend): sliding-window
+PagedAttention" (#116), "Verification": one sequence ends in 5 query tokens
+at context length 300, the other decodes a single token at context length
+40; windows 16, 100 and 4096; head dims 64 and 66.  Values are synthetic
+(seeded N(0, 1)); the pages print none.
 """
 
 from dataclasses import replace
