@@ -272,6 +272,8 @@ def decode(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, scale, 
     """
     import torch
     _validate(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, num_kv_heads, block_size)
+    if q.shape[0] == 0:
+        return out          # no query token in the batch: nothing to compute, nothing to call
     if max_query_len is None:
         max_query_len = int(q.shape[0]) if block_tables.shape[0] else 1
         max_query_len = max(1, min(max_query_len, int(max_seq_len)))
@@ -345,6 +347,7 @@ class Prepared:
         self.workspace = workspace
         self._keep = (out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, k_scale, v_scale,
                       q_scale)
+        self._empty = q.shape[0] == 0
         vp = ctypes.c_void_p
         self.args = (
             vp(out.data_ptr()), vp(q.data_ptr()), vp(k_cache.data_ptr()), vp(v_cache.data_ptr()),
@@ -365,6 +368,8 @@ class Prepared:
         self.opts.event_end = _event_handle(event_end)
 
     def __call__(self):
+        if self._empty:
+            return          # no query token in the batch
         st = self._fn(*self.args)
         if st:
             _check(st)

@@ -201,7 +201,10 @@ pa_status pa_decode_workspace_size_ex(const pa_dims* dims, int32_t window, int32
 
 /*
  * Paged-attention decode: writes out[T, H_q, D].
- *   out, q, k_cache, v_cache   device pointers, 16-byte aligned, layouts above
+ *   out, q, k_cache, v_cache   device pointers, non-NULL, 16-byte aligned,
+ *              layouts above (the library cannot see T on the host: a
+ *              caller whose batch has no query tokens at all, T = 0, has
+ *              nothing to compute and need not call)
  *   block_tables, seq_lens, query_lens   device int32 arrays, 4-byte aligned
  *   scale      finite logit scale
  *   window     0 (unlimited causal) or the window length in positions

@@ -111,6 +111,23 @@ def test_max_rows_and_edge_lengths():
                             BF16_TOL, f"edges D={D} w={win} path={path} sched={sched} P={P}")
 
 
+def test_batch_without_query_tokens():
+    """Every query_lens[b] = 0: no output rows (T = 0), and the call through the
+    binding and a prepared call both return without error."""
+    w = small(4, batch=3, seq_lens=(251, 40, 7), query_lens=(0, 0, 0), query_len=2,
+              block_size=16, max_seq_len=251, max_blocks_per_seq=17)
+    for win in (0, 5):
+        c = workloads.make_case(w, device="cuda", window=win)
+        assert c.q.shape[0] == 0
+        out = run_gpu(c)
+        assert out.shape[0] == 0
+        call = pa.Prepared(out, c.q, c.k_cache, c.v_cache, c.block_tables, c.seq_lens,
+                           c.query_lens, c.scale, win, w.num_kv_heads, w.block_size,
+                           w.max_seq_len, w.query_len)
+        call()
+        torch.cuda.synchronize()
+
+
 def test_debug_spans_bit_exact():
     for name in workloads.WORKLOADS:
         w = workloads.WORKLOADS[name]
