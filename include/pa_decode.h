@@ -200,7 +200,8 @@ pa_status pa_decode_workspace_size_ex(const pa_dims* dims, int32_t window, int32
                                       int32_t block_size, const pa_options* opts, size_t* bytes);
 
 /*
- * Paged-attention decode: writes out[T, H_q, D].
+ * Paged-attention decode: writes out[T, H_q, D].  With the environment
+ * variable PA_LOG set (and not "0"), each call prints its plan to stderr.
  *   out, q, k_cache, v_cache   device pointers, non-NULL, 16-byte aligned,
  *              layouts above (the library cannot see T on the host: a
  *              caller whose batch has no query tokens at all, T = 0, has
