@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <string>
 
 #include "pa_common.h"
@@ -265,23 +266,24 @@ pa_status device_cu_count(int* out) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-// Resident workgroups of a kernel on the current device (cached per kernel).
+// Resident workgroups of a kernel on the current device (workgroups per CU
+// cached per kernel; the kernels are the same code on every gfx950 device).
 int resident_wgs(const void* fn, int threads, int cus) {
-  static std::atomic<int> cache[64];
-  static std::atomic<const void*> keys[64];
-  for (int i = 0; i < 64; ++i) {
-    if (keys[i].load() == fn) return cache[i].load() * cus;
-    if (keys[i].load() == nullptr) {
-      int per_cu = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0) != hipSuccess ||
-          per_cu < 1)
-        per_cu = 1;
-      cache[i].store(per_cu);
-      keys[i].store(fn);
-      return per_cu * cus;
-    }
+  static std::mutex lock;
+  static const void* keys[64];
+  static int per_cu_of[64];
+  std::lock_guard<std::mutex> guard(lock);
+  int i = 0;
+  for (; i < 64 && keys[i] != nullptr; ++i)
+    if (keys[i] == fn) return per_cu_of[i] * cus;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  if (i < 64) {
+    keys[i] = fn;
+    per_cu_of[i] = per_cu;
   }
-  return cus;
+  return per_cu * cus;
 }
 
 // Stream of a call and the caller's timing events.  With events, the
@@ -394,11 +396,13 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
                 (unsigned long long)p.workspace_bytes);
   if (log_enabled())
     std::fprintf(stderr,
-                 "[pa_decode] B=%d Hq=%d Hkv=%d D=%d bs=%d w=%d kv8=%d R=%d span_max=%d path=%s P=%d NP=%d "
-                 "waves=%d one_shot=%d persistent=%d streaming=%d ws=%llu cus=%d\n",
-                 d->batch, d->num_q_heads, hkv, d->head_dim, bs, window, (int)kv8, p.rows, p.span_max,
-                 p.path == PA_PATH_MFMA ? "mfma" : "valu", p.part_size, p.num_parts, p.waves,
-                 p.one_shot, p.persistent, p.streaming, (unsigned long long)p.workspace_bytes, cus);
+                 "[pa_decode] B=%d Hq=%d Hkv=%d D=%d bs=%d w=%d kv8=%d q8=%d R=%d span_max=%d path=%s "
+                 "P=%d NP=%d waves=%d row_tiles=%d row_blocks=%d one_shot=%d persistent=%d "
+                 "streaming=%d ws=%llu cus=%d\n",
+                 d->batch, d->num_q_heads, hkv, d->head_dim, bs, window, (int)kv8, (int)q8, p.rows,
+                 p.span_max, p.path == PA_PATH_MFMA ? "mfma" : "valu", p.part_size, p.num_parts,
+                 p.waves, p.row_tiles, p.row_blocks, p.one_shot, p.persistent, p.streaming,
+                 (unsigned long long)p.workspace_bytes, cus);
 
   const uint64_t states = (uint64_t)d->batch * hkv * p.num_parts * p.rows;
   char* ws = (char*)workspace;

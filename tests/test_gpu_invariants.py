@@ -239,3 +239,39 @@ def test_timing_events_change_nothing(path, sched):
     kern = kb.elapsed_time(ke)
     assert 0 < kern <= cb.elapsed_time(ce)
     assert cb.elapsed_time(kb) >= 0 and ke.elapsed_time(ce) >= 0
+
+
+def test_concurrent_calls_from_threads():
+    """Calls are reentrant: four host threads, each with its own stream, output
+    and workspace, run the same calls (both schedules, several plans) at the
+    same time and get bit-identical outputs to a single-threaded run."""
+    import threading
+    w = workloads.WORKLOADS["gqa_bf16"]
+    c = workloads.make_case(replace(w, batch=6), device="cuda", window=0)
+    plans = [dict(schedule=pa.SCHED_PERSISTENT), dict(schedule=pa.SCHED_GRID, part_size=256),
+             dict(schedule=pa.SCHED_PERSISTENT, part_size=128), dict(path=pa.PATH_VALU)]
+    ref_out = [run_gpu(c, **o).clone() for o in plans]
+    results, errors = [None] * len(plans), []
+
+    def worker(k):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                out = c.new_out()
+                for _ in range(5):
+                    pa.decode(out, c.q, c.k_cache, c.v_cache, c.block_tables, c.seq_lens,
+                              c.query_lens, c.scale, 0, w.num_kv_heads, w.block_size,
+                              max_seq_len=w.max_seq_len, max_query_len=1, stream=s, **plans[k])
+                s.synchronize()
+            results[k] = out
+        except Exception as e:  # reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(len(plans))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not errors, errors
+    for k in range(len(plans)):
+        assert torch.equal(results[k].view(torch.int16), ref_out[k].view(torch.int16)), plans[k]
