@@ -22,7 +22,7 @@ import os
 
 __all__ = [
     "PaError", "Dims", "Plan", "Options", "load", "library_path", "plan", "workspace_size",
-    "decode", "debug_spans", "PATH_AUTO", "PATH_VALU", "PATH_MFMA", "F32", "BF16",
+    "decode", "debug_spans", "check_inputs", "PATH_AUTO", "PATH_VALU", "PATH_MFMA", "F32", "BF16",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -35,7 +35,8 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 
 EXPORTED_SYMBOLS = (
     "pa_plan_compute", "pa_decode_workspace_size", "pa_decode_workspace_size_ex",
-    "pa_decode", "pa_decode_ex", "pa_debug_spans", "pa_status_string", "pa_last_error",
+    "pa_decode", "pa_decode_ex", "pa_debug_spans", "pa_check_inputs", "pa_status_string",
+    "pa_last_error",
 )
 
 
@@ -101,12 +102,13 @@ def load() -> ctypes.CDLL:
                               ctypes.c_size_t, P]
     lib.pa_decode_ex.argtypes = lib.pa_decode.argtypes + [po]
     lib.pa_debug_spans.argtypes = [P, P, P, I32, I32, I32, pd, po, P, P, P, P, P]
+    lib.pa_check_inputs.argtypes = [P, P, P, I32, I32, I32, pd, P, P]
     lib.pa_status_string.argtypes = [I32]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_last_error.argtypes = []
     lib.pa_last_error.restype = ctypes.c_char_p
     for name in ("pa_plan_compute", "pa_decode_workspace_size", "pa_decode_workspace_size_ex",
-                 "pa_decode", "pa_decode_ex", "pa_debug_spans"):
+                 "pa_decode", "pa_decode_ex", "pa_debug_spans", "pa_check_inputs"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -373,3 +375,22 @@ class Prepared:
         st = self._fn(*self.args)
         if st:
             _check(st)
+
+
+def check_inputs(block_tables, seq_lens, query_lens, window, num_kv_heads, block_size, dims: Dims,
+                 stream=None) -> dict:
+    """Device-side precondition report of a call's lengths and block tables
+    (see pa_check_inputs); waits for the stream."""
+    import torch
+    report = torch.empty(4, dtype=torch.int32, device=block_tables.device)
+    s = _stream_handle(stream)
+    _check(load().pa_check_inputs(
+        ctypes.c_void_p(block_tables.data_ptr()), ctypes.c_void_p(seq_lens.data_ptr()),
+        ctypes.c_void_p(query_lens.data_ptr()), int(window), int(num_kv_heads), int(block_size),
+        ctypes.byref(dims), ctypes.c_void_p(report.data_ptr()), s))
+    (stream or torch.cuda.current_stream()).synchronize()
+    r = report.cpu().tolist()
+    none = 0x7fffffff
+    return dict(bad_lengths=r[0], bad_entries=r[1],
+                first_bad_sequence=None if r[2] == none else r[2],
+                first_bad_entry=None if r[3] == none else r[3])

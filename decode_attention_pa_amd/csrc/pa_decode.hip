@@ -592,6 +592,38 @@ pa_status pa_debug_spans(const int32_t* block_tables, const int32_t* seq_lens,
   return PA_OK;
 }
 
+pa_status pa_check_inputs(const int32_t* block_tables, const int32_t* seq_lens,
+                          const int32_t* query_lens, int32_t window, int32_t num_kv_heads,
+                          int32_t block_size, const pa_dims* dims, int32_t* report,
+                          void* hip_stream) {
+  pa_status st = check_shape(dims, window, num_kv_heads, block_size);
+  if (st != PA_OK) return st;
+  if (!block_tables || !seq_lens || !query_lens || !report)
+    return fail(PA_ERR_INVALID_ARG, "a pointer is NULL");
+  if (!aligned(block_tables, 4) || !aligned(seq_lens, 4) || !aligned(query_lens, 4) ||
+      !aligned(report, 4))
+    return fail(PA_ERR_INVALID_ARG, "int32 arrays must be 4-byte aligned");
+  const hipStream_t s = (hipStream_t)hip_stream;
+  hipLaunchKernelGGL(pa::check_init, dim3(1), dim3(64), 0, s, report);
+  if (dims->batch > 0) {
+    pa::CheckArgs a = {};
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.query_lens = query_lens;
+    a.report = report;
+    a.window = window;
+    a.log2_bs = ilog2_exact(block_size);
+    a.max_blocks_per_seq = dims->max_blocks_per_seq;
+    a.max_seq_len = dims->max_seq_len;
+    a.max_query_len = dims->max_query_len;
+    a.num_blocks = dims->num_blocks;
+    hipLaunchKernelGGL(pa::check_inputs, dim3(dims->batch), dim3(64), 0, s, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "check_inputs launch");
+  return PA_OK;
+}
+
 const char* pa_status_string(pa_status s) {
   switch (s) {
     case PA_OK: return "PA_OK";

@@ -185,4 +185,50 @@ __global__ __launch_bounds__(64) void debug_spans(SpanArgs a) {
   }
 }
 
+// Precondition check (debug aid).  report = {bad length sequences, bad table
+// entries, first bad sequence, first bad entry}; check_init clears it on the
+// stream first (a kernel, so that the pair can sit in a captured graph).
+struct CheckArgs {
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const int32_t* query_lens;
+  int32_t* report;
+  int window;
+  int log2_bs;
+  int max_blocks_per_seq;
+  int max_seq_len;
+  int max_query_len;
+  int num_blocks;
+};
+
+__global__ __launch_bounds__(64) void check_init(int32_t* report) {
+  if (threadIdx.x < 4) report[threadIdx.x] = threadIdx.x < 2 ? 0 : 0x7fffffff;
+}
+
+// One wave per sequence.
+__global__ __launch_bounds__(64) void check_inputs(CheckArgs a) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int L = a.seq_lens[b], q = a.query_lens[b];
+  if (q < 0 || L < 0 || q > L || L > a.max_seq_len || q > a.max_query_len) {
+    if (lane == 0) {
+      atomicAdd(&a.report[0], 1);
+      atomicMin(&a.report[2], b);
+    }
+    return;
+  }
+  if (q == 0) return;  // no row: no position is visible
+  // union of the rows' visible ranges: [first visible of row 0, L)
+  const int k0 = first_visible(L, q, 0, a.window) >> a.log2_bs;
+  const int k1 = min((L - 1) >> a.log2_bs, a.max_blocks_per_seq - 1);
+  const int32_t* row = a.block_tables + (size_t)b * a.max_blocks_per_seq;
+  for (int k = k0 + lane; k <= k1; k += 64) {
+    const int id = row[k];
+    if (id < 0 || id >= a.num_blocks) {
+      atomicAdd(&a.report[1], 1);
+      const long long at = (long long)b * a.max_blocks_per_seq + k;
+      atomicMin(&a.report[3], (int)min(at, 0x7ffffffeLL));
+    }
+  }
+}
+
 }  // namespace pa

@@ -247,6 +247,32 @@ pa_status pa_debug_spans(const int32_t* block_tables, const int32_t* seq_lens,
                          int32_t* seq_info, int32_t* row_info, int32_t* blocks,
                          int32_t* parts, void* hip_stream);
 
+/*
+ * Debug aid, off the hot path: checks on the device the preconditions
+ * pa_decode relies on but cannot see from the host (the lengths and the
+ * block-table rows of the call, as gllm #116 "What changes — Interface"
+ * passes them), so that a caller can have bad inputs reported instead of
+ * read (executorch PR #18759 review: arguments the kernel cannot serve
+ * should fail clearly).  Writes into `report`, a caller-owned device
+ * int32[4]:
+ *   report[0]  sequences with q_b < 0, L_b < 0, q_b > L_b, L_b > max_seq_len
+ *              or q_b > max_query_len
+ *   report[1]  block-table entries outside [0, num_blocks) among those of
+ *              logical blocks that hold a visible position of their sequence
+ *   report[2]  smallest b counted in report[0], INT32_MAX if none
+ *   report[3]  smallest b * max_blocks_per_seq + k counted in report[1],
+ *              INT32_MAX if none
+ * Sequences counted in report[0] are not scanned for table entries.  The
+ * kernels read seq_lens, query_lens and only table entries k <
+ * min(ceil(L_b / block_size), max_blocks_per_seq); read `report` once the
+ * stream has completed the call.  Host-visible arguments are validated as
+ * for pa_decode.
+ */
+pa_status pa_check_inputs(const int32_t* block_tables, const int32_t* seq_lens,
+                          const int32_t* query_lens, int32_t window, int32_t num_kv_heads,
+                          int32_t block_size, const pa_dims* dims, int32_t* report,
+                          void* hip_stream);
+
 /* Static description of a status code. */
 const char* pa_status_string(pa_status status);
 

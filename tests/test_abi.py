@@ -330,3 +330,11 @@ def test_fp8_query_format_rules(lib):
         with pytest.raises(pa.PaError) as e:
             pa.plan(dims_of(w, **over), 0, 8, 16, **kw)
         assert e.value.status == code, over
+
+
+def test_check_inputs_rejects_null_pointers(lib):
+    d = pa.make_dims(2, 4, 64, 1, 64, 4, 16, pa.BF16)
+    z = ctypes.c_void_p(16)
+    for args in ((None, z, z, z), (z, None, z, z), (z, z, None, z), (z, z, z, None)):
+        st = lib.pa_check_inputs(args[0], args[1], args[2], 0, 1, 16, ctypes.byref(d), args[3], None)
+        assert st == pa.ERR_INVALID_ARG
