@@ -1,4 +1,5 @@
-// Partition kernel on bf16 matrix cores (gfx950 v_mfma_f32_16x16x32_bf16).
+// Partition kernel on the matrix cores (gfx950 v_mfma_f32_16x16x32_bf16; for
+// FP8 queries over an FP8 cache, QK^T on v_mfma_f32_16x16x32_fp8_fp8).
 //
 // One workgroup = NW waves = one context partition of one (sequence, KV
 // head).  The G*q_b query rows of the KV head are packed as the N dimension
@@ -23,6 +24,12 @@
 // 8*lg + 4*t + j, so after QK each lane group lg owns the 8 consecutive
 // positions 8*lg .. 8*lg+7 of its row: exactly the B-operand slice PV needs,
 // with no data movement between the two products.
+//
+// FP8 caches (KV8): E4M3 codes are loaded as they are (16 dims of K per
+// 16-byte load) and converted to bf16 in registers, exactly; the K scale
+// joins the logit scale and the V scale the final normalisation.  FP8
+// queries (Q8, with KV8 only): Q is loaded as codes and QK^T multiplies code
+// by code on the FP8 matrix cores; the Q scale joins the logit scale.
 //
 // Split-K (executorch PR #18759, "split-K flash-decoding"; aiter PR #2914,
 // workspace max_logits / exp_sums / temporary_output): a sequence with one
