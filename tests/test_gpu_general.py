@@ -152,3 +152,26 @@ def test_merge_lanes_with_partial_unit_blocks(D, dtype):
             say(f"[case] merge odd units D={D} {dtype} w={win} P={P}")
             compare(run_gpu(c, part_size=P), exp, rows, tol,
                     f"merge odd D={D} {dtype} w={win} P={P}")
+
+
+MAX_ROWS = [(64, "bf16", ""), (128, "bf16", ""), (256, "bf16", ""), (128, "bf16", "fp8"),
+            (64, "f32", "")]
+
+
+@pytest.mark.parametrize("D,dtype,kv", MAX_ROWS,
+                         ids=[f"d{d}-{t}{'-' + k if k else ''}" for d, t, k in MAX_ROWS])
+def test_maximum_rows(D, dtype, kv):
+    """1024 packed rows per KV head, the most the library takes (G = 8 and 128
+    query tokens): 16 to 64 row blocks per partition."""
+    w = workloads.custom(
+        name=f"rows1024_d{D}_{dtype}{kv}", dtype=dtype, kv_dtype=kv, batch=2, num_q_heads=16,
+        num_kv_heads=2, head_dim=D, block_size=16, query_len=128, query_lens=(128, 77),
+        seq_lens=(300, 150), max_seq_len=300, max_blocks_per_seq=20, pool=0, seed=1024 + D,
+        scale=float(1.0 / np.sqrt(D)), windows=(0,))
+    tol = BF16_TOL if dtype == "bf16" else F32_TOL
+    for win in (0, 50):
+        c = workloads.make_case(w, device="cuda", window=win)
+        exp, rows = oracle_out(c)
+        for P in (0, 64):
+            say(f"[case] 1024 rows D={D} {dtype} kv={kv} w={win} P={P}")
+            compare(run_gpu(c, part_size=P), exp, rows, tol, f"1024 rows D={D} {dtype} w={win} P={P}")
