@@ -13,7 +13,10 @@
   run, give bit-identical outputs;
 * query heads of one group with identical query vectors give identical
   outputs; one partition versus many agree to bf16 resolution at the scale
-  of each output row (2^-6 of the row's largest magnitude).
+  of each output row (2^-6 of the row's largest magnitude);
+* a window at least as long as the context equals window 0, and a GQA call
+  equals an MHA call over repeated KV heads, bit for bit; an MTP row equals
+  the one-token call whose context ends at that row.
 """
 
 from dataclasses import replace
@@ -275,3 +278,55 @@ def test_concurrent_calls_from_threads():
     assert not errors, errors
     for k in range(len(plans)):
         assert torch.equal(results[k].view(torch.int16), ref_out[k].view(torch.int16)), plans[k]
+
+
+@pytest.mark.parametrize("path,sched", KERNELS)
+def test_window_at_least_context_equals_no_window(path, sched):
+    """A window at least as long as every context sees what window 0 sees;
+    the plans coincide, so the outputs are bit-identical."""
+    w = mtp_workload()
+    for big in (w.max_seq_len, w.max_seq_len + 7, 1 << 20):
+        c0 = workloads.make_case(w, device="cuda", window=0)
+        cw = workloads.make_case(w, device="cuda", window=big)
+        a = run_gpu(c0, path=path, schedule=sched).clone()
+        b = run_gpu(cw, path=path, schedule=sched)
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), (path, sched, big)
+
+
+@pytest.mark.parametrize("window", [0, 5])
+def test_mtp_row_equals_shorter_single_token_call(window):
+    """Query token i of a q-token call equals a one-token call whose context
+    ends at that token (L' = L - (q - 1 - i)), same cache and query vector."""
+    w = mtp_workload(query_len=4, seq_lens=(150, 77))
+    c = workloads.make_case(w, device="cuda", window=window)
+    full = run_gpu(c).float()
+    q_b = w.query_len
+    for i in range(q_b):
+        rows = [b * q_b + i for b in range(w.batch)]
+        lens = torch.tensor([L - (q_b - 1 - i) for L in w.seq_lens], dtype=torch.int32, device="cuda")
+        ones = torch.ones(w.batch, dtype=torch.int32, device="cuda")
+        q1 = c.q[rows].contiguous()
+        out1 = torch.empty_like(q1)
+        pa.decode(out1, q1, c.k_cache, c.v_cache, c.block_tables, lens, ones, c.scale, window,
+                  w.num_kv_heads, w.block_size, max_seq_len=w.max_seq_len, max_query_len=1)
+        torch.cuda.synchronize()
+        diff = (out1.float() - full[rows]).abs().max().item()
+        assert diff <= 8e-3, (i, window, diff)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_gqa_equals_mha_with_repeated_heads(path):
+    """G = 4 query heads per KV head give bit for bit what G = 1 gives with
+    each KV head repeated for its group (rows are computed independently;
+    the same grid plan on both sides)."""
+    w = mtp_workload(num_q_heads=8, num_kv_heads=2, query_len=2, seq_lens=(150, 77))
+    c = workloads.make_case(w, device="cuda", window=0)
+    gqa = run_gpu(c, path=path, schedule=pa.SCHED_GRID, part_size=64).clone()
+    k8 = c.k_cache.repeat_interleave(4, dim=1).contiguous()
+    v8 = c.v_cache.repeat_interleave(4, dim=1).contiguous()
+    mha = torch.empty_like(gqa)
+    pa.decode(mha, c.q, k8, v8, c.block_tables, c.seq_lens, c.query_lens, c.scale, 0, 8,
+              w.block_size, max_seq_len=w.max_seq_len, max_query_len=w.query_len, path=path,
+              schedule=pa.SCHED_GRID, part_size=64)
+    torch.cuda.synchronize()
+    assert torch.equal(gqa.view(torch.int16), mha.view(torch.int16))
