@@ -134,7 +134,9 @@ pa_status make_plan(const pa_dims* d, int32_t window, int32_t hkv, int32_t bs, i
   if (r.path == PA_PATH_MFMA) {
     // Row tiles (16 rows each) per workgroup: all rows when they fit in 64
     // (D = 256: one tile, for registers); beyond that blocks of 64 rows at
-    // D = 64 and 32 rows at D = 128, which keep 3-4 waves per SIMD.
+    // D = 64 and 32 rows at D = 128 (2 waves per SIMD at 212 VGPRs, and still
+    // faster on MI355X than one-tile blocks, which read K/V twice as often:
+    // 61 against 66-70 us on a 128-row batch).
     const int need = (r.rows + 15) / 16;
     const int cap = d->head_dim == 256 ? 1 : (r.rows <= 64 ? 4 : (d->head_dim == 64 ? 4 : 2));
     r.row_tiles = std::min(need, cap);
