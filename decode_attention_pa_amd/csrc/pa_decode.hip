@@ -222,18 +222,21 @@ pa_status make_plan(const pa_dims* d, int32_t window, int32_t hkv, int32_t bs, i
   r.one_shot = r.num_parts == 1;
   if (r.one_shot && sched_req != 2) r.persistent = 0;
   const int w_req = o ? o->waves : 0;
-  if (r.path == PA_PATH_MFMA && !r.persistent && w_req == 0) {
-    // Grid plans with few waves in flight.  One-shot with under 16 waves
-    // per CU: rows in one-tile blocks of 4 waves (measured on MI355X: 512
+  if (r.path == PA_PATH_MFMA && w_req == 0) {
+    // Grid plans with few waves in flight, one-shot with under 16 waves per
+    // CU: rows in one-tile blocks of 4 waves (measured on MI355X: 512
     // sliding-window MTP units of 32 rows, 10 % faster per call as 1024
-    // workgroups x 4 waves than as 512 x 2).  Split at head dim 256: 2 waves
-    // (a long single sequence, 15 % faster than 4).
-    if (r.one_shot && r.row_tiles > 1 && d->head_dim != 256 &&
+    // workgroups x 4 waves than as 512 x 2).
+    if (!r.persistent && r.one_shot && r.row_tiles > 1 && d->head_dim != 256 &&
         units * r.row_blocks * r.waves < 16 * (int64_t)num_cus) {
       r.row_tiles = 1;
       r.waves = 4;
       r.row_blocks = (r.rows + 15) / 16;
     }
+    // Split plans at head dim 256 (~250 VGPRs, one or two waves per SIMD):
+    // 2 waves per workgroup, so that twice as many workgroups share the CUs
+    // (a long single sequence: 15 % faster than 4 waves; a 32-sequence GQA
+    // batch on the persistent schedule: 5 %).
     if (!r.one_shot && d->head_dim == 256) r.waves = 2;
   }
   const bool reread = r.row_blocks > 1;

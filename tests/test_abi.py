@@ -134,7 +134,7 @@ def test_general_rows_and_head_dims(lib):
     p = pa.plan(dims_of(w, max_query_len=256, head_dim=64), 0, 8, 16)   # 1024 rows
     assert (p["row_tiles"], p["row_blocks"], p["waves"]) == (4, 16, 1)
     p = pa.plan(dims_of(w, max_query_len=3, head_dim=256), 0, 8, 16)    # 12 rows, D = 256
-    assert (p["path"], p["row_tiles"], p["row_blocks"], p["waves"]) == (pa.PATH_MFMA, 1, 1, 4)
+    assert (p["path"], p["row_tiles"], p["row_blocks"], p["waves"]) == (pa.PATH_MFMA, 1, 1, 2)
     p = pa.plan(dims_of(w, max_query_len=5, head_dim=256), 0, 8, 16)    # 20 rows, D = 256
     assert (p["row_tiles"], p["row_blocks"]) == (1, 2)
     p = pa.plan(dims_of(w, head_dim=66), 0, 8, 16)                   # odd head dim
@@ -307,10 +307,14 @@ def test_grid_plans_with_few_waves(lib):
     assert (p["row_tiles"], p["row_blocks"], p["waves"]) == (2, 1, 2)
     p = pa.plan(dims_of(swa), 128, 8, 64, num_cus=256, waves=2)
     assert (p["row_tiles"], p["row_blocks"], p["waves"]) == (2, 1, 2)
-    # head dim 256, one long sequence: 4-chunk partitions and 2 waves
+    # head dim 256, one long sequence: 4-chunk partitions and 2 waves; a batch
+    # on the persistent schedule takes 2 waves too
     d256 = workloads.WORKLOADS["d256_decode_bf16"]
     p = pa.plan(dims_of(d256), 0, 2, 16, num_cus=256)
     assert (p["part_size"], p["waves"], p["persistent"]) == (128, 2, 0)
+    b256 = workloads.WORKLOADS["gqa_d256_bf16"]
+    p = pa.plan(dims_of(b256), 0, 2, 16, num_cus=256)
+    assert (p["waves"], p["persistent"]) == (2, 1)
 
 
 def test_fp8_query_format_rules(lib):

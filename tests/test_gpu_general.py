@@ -106,7 +106,7 @@ def test_head_dim_256_small(seed, kv):
                         f"d256 small{seed} kv={kv} w={win} sched={sched} P={P}")
 
 
-@pytest.mark.parametrize("name", ["d256_decode_bf16", "prefill_chunk_bf16"])
+@pytest.mark.parametrize("name", ["d256_decode_bf16", "gqa_d256_bf16", "prefill_chunk_bf16"])
 def test_general_workloads(name):
     w = workloads.WORKLOADS[name]
     c = workloads.make_case(w, device="cuda")

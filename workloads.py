@@ -124,6 +124,12 @@ WORKLOADS = {
         description="head-dim-256 decode bf16 (the split-K decode benchmark shape of "
                     "executorch PR #18759: B=1, 16/2 heads, D=256), bs=16, context 16384, "
                     "q_len 1"),
+    "gqa_d256_bf16": Workload(
+        name="gqa_d256_bf16", dtype="bf16", batch=32, num_q_heads=16, num_kv_heads=2,
+        head_dim=256, block_size=16, query_len=1, windows=(0,), scale=1.0 / 16.0, seed=9,
+        max_blocks_per_seq=512, max_seq_len=8192, len_range=(512, 8192),
+        description="GQA decode bf16 at head dim 256: B=32, 16/2 heads, D=256, bs=16, "
+                    "context U[512, 8192], q_len 1, window 0"),
     "prefill_chunk_bf16": Workload(
         name="prefill_chunk_bf16", dtype="bf16", batch=16, num_q_heads=32, num_kv_heads=4,
         head_dim=128, block_size=16, query_len=16, windows=(0,),
