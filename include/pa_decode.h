@@ -81,7 +81,7 @@ extern "C" {
 typedef enum pa_status {
   PA_OK = 0,
   PA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad size or shape */
-  PA_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement */
+  PA_ERR_UNSUPPORTED = 2,   /* valid request the library does not implement */
   PA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
   PA_ERR_HIP = 4            /* a HIP runtime call failed (message has the HIP error) */
 } pa_status;
