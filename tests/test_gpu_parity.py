@@ -111,6 +111,31 @@ def test_max_rows_and_edge_lengths():
                             BF16_TOL, f"edges D={D} w={win} path={path} sched={sched} P={P}")
 
 
+@pytest.mark.parametrize("B,sched", [(1024, pa.SCHED_PERSISTENT), (1100, pa.SCHED_AUTO)])
+def test_largest_batches(B, sched):
+    """The persistent schedule's largest batch (1024 sequences, its prefix sums
+    in shared memory) and a larger one, which the plan hands to the grid
+    schedule.  Query lengths 0-3 make every row offset a long prefix sum;
+    sampled sequences include the last ones."""
+    r = np.random.default_rng(B)
+    qls = tuple(int(x) for x in r.integers(0, 4, size=B))
+    lens = tuple(int(q + x) for q, x in zip(qls, r.integers(1, 400, size=B)))
+    w = small(5, batch=B, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+              query_len=3, seq_lens=lens, query_lens=qls, max_seq_len=max(lens),
+              max_blocks_per_seq=-(-max(lens) // 16) + 1)
+    pick = sorted(set(int(x) for x in r.choice(B, size=40, replace=False)) | {0, B - 2, B - 1})
+    for win in (0, 33):
+        c = workloads.make_case(w, device="cuda", window=win)
+        say(f"[case] batch {B} window={win} schedule={sched}")
+        exp, rows = oracle_out(c, pick)
+        # the larger batch is one-shot as planned; 64-position partitions
+        # split it and send every sequence through the merge as well
+        for P in ((0,) if sched == pa.SCHED_PERSISTENT else (0, 64)):
+            out = run_gpu(c, schedule=sched, part_size=P)
+            compare(out, exp, rows, BF16_TOL, f"batch {B} w={win} sched={sched} P={P}")
+            assert torch.isfinite(out.float()).all()
+
+
 def test_batch_without_query_tokens():
     """Every query_lens[b] = 0: no output rows (T = 0), and the call through the
     binding and a prepared call both return without error."""
