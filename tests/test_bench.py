@@ -1,0 +1,76 @@
+"""bench.py's accounting, on the CPU.
+
+The roofline figure divides the partition kernel's algorithmic bytes by its
+duration; here those bytes are checked against a count made position by
+position from the oracle's visibility rule (K and V of every position some
+row of a (sequence, KV head) sees, the table entries of the blocks holding
+them, Q and the two length arrays).  Also: more than one GPU is refused
+before anything touches a device.
+"""
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+import workloads
+from oracle import paged_attention as ref
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def counted_bytes(case):
+    w = case.w
+    s = 2 if w.dtype == "bf16" else 4
+    skv = 1 if w.kv_dtype == "fp8" else s
+    sq = 1 if w.q_dtype == "fp8" else s
+    kv = tables = 0
+    for L, q in zip(case.seq_lens_host, case.query_lens_host):
+        seen = set()
+        for i in range(q):
+            lo, p = ref.visible_range(L, q, i, case.window)
+            seen.update(range(lo, p + 1))
+        kv += len(seen) * w.num_kv_heads * w.head_dim * 2 * skv
+        tables += 4 * len({t // w.block_size for t in seen})
+    T = sum(case.query_lens_host)
+    return dict(kv=kv, tables=tables, q=T * w.num_q_heads * w.head_dim * sq,
+                out=T * w.num_q_heads * w.head_dim * s, lens=8 * w.batch)
+
+
+def _cases():
+    yield workloads.make_case("tiny_f32", device="cpu", window=0)
+    yield workloads.make_case("tiny_f32", device="cpu", window=5)
+    mtp = workloads.custom(name="mtp", dtype="bf16", batch=5, num_q_heads=8, num_kv_heads=2,
+                           head_dim=64, block_size=16, query_len=4,
+                           seq_lens=(1, 17, 40, 300, 301), query_lens=(1, 4, 0, 3, 4),
+                           max_seq_len=301, max_blocks_per_seq=20, pool=0, seed=7,
+                           scale=0.125, windows=(0,))
+    for win in (0, 1, 2, 16, 33, 1000):
+        yield workloads.make_case(mtp, device="cpu", window=win)
+    fp8 = workloads.custom(name="fp8", dtype="bf16", kv_dtype="fp8", q_dtype="fp8", batch=3,
+                           num_q_heads=4, num_kv_heads=1, head_dim=128, block_size=32,
+                           query_len=2, seq_lens=(70, 5, 129), max_seq_len=129,
+                           max_blocks_per_seq=6, pool=0, seed=8, scale=0.08, windows=(0,))
+    for win in (0, 7):
+        yield workloads.make_case(fp8, device="cpu", window=win)
+
+
+@pytest.mark.parametrize("case", list(_cases()), ids=lambda c: f"{c.w.name}-w{c.window}")
+def test_algorithmic_bytes_match_a_position_count(case):
+    got = bench.algorithmic_bytes(case)
+    exp = counted_bytes(case)
+    for k, v in exp.items():
+        assert got[k] == v, (k, got[k], v)
+    assert got["partition_kernel"] == exp["kv"] + exp["q"] + exp["tables"] + exp["lens"]
+    assert got["total"] == got["partition_kernel"] + exp["out"]
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120,
+                       env=dict(os.environ, HIP_VISIBLE_DEVICES=""))
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
