@@ -102,34 +102,44 @@ def _counter_rows(path):
                 yield from csv.DictReader(open(os.path.join(root, f)))
 
 
+def counter_bytes(rows, name: str) -> dict:
+    """HBM bytes per partition-kernel launch from one counter's rows
+    ((dispatch id, kernel name, KiB) per dispatch, any order): the counter
+    is scaled by what it reads for the plain 1 GiB device copies issued right
+    before the first partition kernel (known to read and write 1 GiB each),
+    and averaged over the partition dispatches after the first (cold) one."""
+    gib_kib = float(1 << 20)
+    rows = sorted(rows)
+    is_part = lambda k: "part_mfma" in k or "part_valu" in k
+    part = [v for _, k, v in rows if is_part(k)]
+    first_part = min((i for i, k, _ in rows if is_part(k)), default=0)
+    # the calibration copies are the last CALIB_COPIES large copies before
+    # the first partition kernel; earlier ones stage the workload's inputs
+    # (of other sizes) and would skew the scale
+    copy = [v for i, k, v in rows
+            if "copyBuffer" in k and v > gib_kib / 8 and i < first_part][-CALIB_COPIES:]
+    if not copy or not part:
+        raise SystemExit(f"{name}: no calibration copy or partition kernel among the dispatches")
+    calib = sum(copy) / len(copy)
+    scale = gib_kib / calib
+    per = sum(part[1:]) / max(len(part) - 1, 1) if len(part) > 1 else part[0]  # first is cold
+    return {"copy_kib": round(calib, 2), "scale": round(scale, 5),
+            "partition_kib_raw": round(per, 2),
+            "partition_bytes": int(per * scale * 1024), "dispatches": len(part)}
+
+
 def ingest_counters(workload: str, window: int, fetch_dir: str, write_dir: str,
                     command: str) -> dict:
     """Turns two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per
     dispatch) of ``bench.py --copy-calibration`` into HBM bytes per launch of
-    the partition kernel.  Each counter is scaled by what it reads for the
-    plain 1 GiB device copy in the same run (known: 1 GiB read, 1 GiB
-    written).  Writes the record into profiles/traffic.json."""
-    gib_kib = float(1 << 20)
+    the partition kernel (``counter_bytes``) and writes the record into
+    profiles/traffic.json."""
     rec = {"workload": workload, "window": window, "kernel_hash": kernel_source_hash(),
            "command": command}
     for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        rows = sorted(((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"]))
-                       for r in _counter_rows(d) if r["Counter_Name"] == name))
-        part = [v for _, k, v in rows if "part_mfma" in k or "part_valu" in k]
-        first_part = min((i for i, k, _ in rows if "part_mfma" in k or "part_valu" in k), default=0)
-        # the calibration copies are the last CALIB_COPIES large copies before
-        # the first partition kernel; earlier ones stage the workload's inputs
-        # (of other sizes) and would skew the scale
-        copy = [v for i, k, v in rows
-                if "copyBuffer" in k and v > gib_kib / 8 and i < first_part][-CALIB_COPIES:]
-        if not copy or not part:
-            raise SystemExit(f"{name}: no calibration copy or partition kernel in {d}")
-        calib = sum(copy) / len(copy)
-        scale = gib_kib / calib
-        per = sum(part[1:]) / max(len(part) - 1, 1) if len(part) > 1 else part[0]  # first is cold
-        rec[name] = {"copy_kib": round(calib, 2), "scale": round(scale, 5),
-                     "partition_kib_raw": round(per, 2),
-                     "partition_bytes": int(per * scale * 1024), "dispatches": len(part)}
+        rows = [(int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"]))
+                for r in _counter_rows(d) if r["Counter_Name"] == name]
+        rec[name] = counter_bytes(rows, name)
     rec["bytes_per_launch"] = rec["FETCH_SIZE"]["partition_bytes"] + rec["WRITE_SIZE"]["partition_bytes"]
     path = os.path.join(ROOT, "profiles", "traffic.json")
     allrec = json.load(open(path)) if os.path.exists(path) else {}

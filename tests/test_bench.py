@@ -74,3 +74,29 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode != 0
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_counter_scaling_uses_the_calibration_copies():
+    """Traffic per launch: the counter scaled by what it reads for the 1 GiB
+    calibration copies issued just before the first partition kernel (input
+    staging copies of other sizes, earlier, are ignored), averaged over the
+    partition dispatches after the cold first one."""
+    gib = float(1 << 20)                                     # KiB
+    rows = [(0, "copyBuffer", 3 * gib),                      # staging, earlier: ignored
+            (1, "copyBuffer", 0.25 * gib),                   # staging: ignored
+            (2, "fill", 7.0),
+            (3, "copyBuffer", 0.5 * gib), (4, "copyBuffer", 0.5 * gib),
+            (5, "copyBuffer", 0.5 * gib),                    # calibration: reads half
+            (6, "pa::part_mfma_ps<...>", 999.0),             # cold first dispatch
+            (7, "pa::lse_reduce<...>", 5.0),
+            (8, "pa::part_mfma_ps<...>", 100.0),
+            (9, "pa::part_mfma_ps<...>", 300.0),
+            (10, "copyBuffer", 8 * gib)]                     # after: ignored
+    rec = bench.counter_bytes(list(reversed(rows)), "FETCH_SIZE")
+    assert rec["scale"] == 2.0
+    assert rec["copy_kib"] == 0.5 * gib
+    assert rec["partition_kib_raw"] == 200.0
+    assert rec["partition_bytes"] == 200 * 2 * 1024
+    assert rec["dispatches"] == 3
+    with pytest.raises(SystemExit):
+        bench.counter_bytes([(0, "pa::part_mfma<...>", 1.0)], "WRITE_SIZE")   # no copy
