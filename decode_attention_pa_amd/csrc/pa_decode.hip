@@ -199,21 +199,33 @@ pa_status make_plan(const pa_dims* d, int32_t window, int32_t hkv, int32_t bs, i
     // each row block as a workgroup, with partitions of 8..128 chunks
     // (4.. at head dim 256: the same K/V bytes per workgroup): longer ones
     // amortise each workgroup's set-up and keep the partial states small,
-    // shorter ones would multiply the LSE merge's work.  One-tile bf16
-    // plans at head dim 128 aim at ~1 workgroup per CU instead: fewer,
-    // longer-running waves (measured on MI355X, flushed: a 131072-position
-    // sequence 15.2 -> 14.9 us and 1.5 us less merge; 4 units of 64k 23.7 ->
-    // 22.6 us; 32 units of 32k 78-80 -> 72.6 us; at head dim 64 and 256 the
-    // finer split stays ahead).  Constants measured on MI355X.
+    // shorter ones would multiply the LSE merge's work.
+    // One-tile plans on the matrix cores size the grid by bytes in flight
+    // instead: each wave has one 32-position chunk of K and V in flight, so
+    // about 64 KB per CU takes 65536 / chunk-bytes waves per CU (4 at head
+    // dim 128 in bf16, 8 over an FP8 cache or at head dim 64, 2 at head dim
+    // 256).  Measured on MI355X, flushed, against the 8-per-CU split: a
+    // 131072-position bf16 sequence 29.5 -> 27.9 us per call; 32 units of
+    // 32k 91-93 -> 84.5 us (bf16) and 47 -> 42 us (FP8); 4 units of 64k
+    // 37.5 -> 36.1 (bf16) and 18.0-18.7 -> 16.0-16.5 us (FP8, kernel).
     const int64_t chunks = cdiv(span_cover, pa::kChunk);
     const int64_t wgs_per_part = std::max<int64_t>(units * r.row_blocks, 1);
-    const bool long_runs = r.path == PA_PATH_MFMA && r.row_tiles == 1 && r.row_blocks == 1 &&
-                           d->head_dim == 128 && d->kv_format == PA_KV_NATIVE;
-    const int64_t per_cu = long_runs ? 1 : 8;
-    const int64_t want = std::max<int64_t>(1, cdiv(per_cu * (int64_t)num_cus, wgs_per_part));
-    // (rounded down on that path, so that the longest unit makes at least
-    // one workgroup per CU: 131072 positions -> 256 partitions of 16 chunks)
-    int64_t pc = long_runs ? std::max<int64_t>(1, chunks / want) : cdiv(chunks, want);
+    const bool by_bytes = r.path == PA_PATH_MFMA && r.row_tiles == 1 && r.row_blocks == 1;
+    int64_t pc;
+    if (by_bytes) {
+      const int64_t chunk_bytes = (int64_t)pa::kChunk * 2 * d->head_dim *
+                                  (d->kv_format == PA_KV_FP8_E4M3 ? 1 : 2);
+      const int64_t waves_per_cu = std::max<int64_t>(1, 65536 / chunk_bytes);
+      const int64_t nw = d->head_dim == 256 ? 2 : r.waves;  // split plans at D = 256 run 2 waves
+      const int64_t wgs = std::max<int64_t>(1, waves_per_cu * num_cus / nw);
+      const int64_t want = std::max<int64_t>(1, cdiv(wgs, wgs_per_part));
+      // rounded down, so that the longest unit fills its share of the CUs
+      // (131072 positions in bf16: 256 partitions of 16 chunks)
+      pc = std::max<int64_t>(1, chunks / want);
+    } else {
+      const int64_t want = std::max<int64_t>(1, cdiv(8 * (int64_t)num_cus, wgs_per_part));
+      pc = cdiv(chunks, want);
+    }
     pc = std::max<int64_t>(pc, d->head_dim == 256 ? 4 : 8);
     pc = std::min<int64_t>(pc, 128);
     r.part_size = (int32_t)(pc * pa::kChunk);
