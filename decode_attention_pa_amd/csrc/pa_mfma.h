@@ -474,8 +474,9 @@ __global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
                                     r0);
 }
 
-// Persistent schedule (aiter PR #2914: "PS" decode): a grid of about one
-// resident set of workgroups.  The partitions of all units form one list,
+// Persistent schedule (aiter PR #2914: "PS" decode): a grid whose
+// workgroups are all resident at once (the launcher picks how many per CU,
+// at most what fits).  The partitions of all units form one list,
 // unit-major ((sequence, KV head), then partition); workgroup w takes the
 // contiguous share [w*I/W, (w+1)*I/W) of the I partitions and runs each
 // unit's stretch of it as one run.  Shares differ by at most one partition,
