@@ -213,8 +213,9 @@ pa_status make_plan(const pa_dims* d, int32_t window, int32_t hkv, int32_t bs, i
     const bool by_bytes = r.path == PA_PATH_MFMA && r.row_tiles == 1 && r.row_blocks == 1;
     int64_t pc;
     if (by_bytes) {
-      const int64_t chunk_bytes = (int64_t)pa::kChunk * 2 * d->head_dim *
-                                  (d->kv_format == PA_KV_FP8_E4M3 ? 1 : 2);
+      const bool kv8 = d->kv_format == PA_KV_FP8_E4M3;
+      const int64_t chunk_bytes = (int64_t)pa::kChunk * 2 * d->head_dim * (kv8 ? 1 : 2) *
+                                  pa::chunks_per_step(d->head_dim, 1, kv8, false);  // bytes per wave step
       const int64_t waves_per_cu = std::max<int64_t>(1, 65536 / chunk_bytes);
       const int64_t nw = d->head_dim == 256 ? 2 : r.waves;  // split plans at D = 256 run 2 waves
       const int64_t wgs = std::max<int64_t>(1, waves_per_cu * num_cus / nw);
@@ -337,7 +338,7 @@ void launch_part(K kernel, dim3 grid, dim3 block, const Launch& L, const pa::Par
 // the GQA batch 89.6-90.1 -> 87.8-88.5 us; FP8 caches best at two).
 template <int D, int NRT, int NW, bool KV8>
 constexpr int ps_wgs_per_cu() {
-  constexpr int chunk_bytes = pa::kChunk * 2 * D * (KV8 ? 1 : 2);
+  constexpr int chunk_bytes = pa::kChunk * 2 * D * (KV8 ? 1 : 2) * pa::chunks_per_step(D, NRT, KV8, true);
   return NRT == 1 ? (65536 / (NW * chunk_bytes) > 1 ? 65536 / (NW * chunk_bytes) : 1) : 1 << 20;
 }
 

@@ -80,6 +80,19 @@ __device__ inline bf16x8 e4m3x8_to_bf16(uint32_t a, uint32_t b) {
 // this (log2 units): weights are then at most 2^8 before normalisation.
 constexpr float kRescaleLog2 = 8.f;
 
+// 32-position chunks a wave takes per loop step.  An FP8 chunk is half the
+// bytes of a bf16 one, so one-tile FP8 waves of the grid schedule up to head
+// dim 128 take two per step: as many bytes in flight per wave as bf16, and
+// one softmax update (max exchange, rescale test) per 64 positions
+// (measured on MI355X, flushed: a 131072-position FP8 sequence 11.8 -> 11.3
+// us, 32 units of 32k 42.1 -> 41.3 us).  The persistent kernel keeps one
+// chunk per step: with two it ran 20 % slower (its waits for a step's
+// second K rows also covered V loads issued after them).  More row tiles,
+// or head dim 256, would lose a wave per SIMD to the extra registers.
+constexpr int chunks_per_step(int D, int NRT, bool kv8, bool persistent) {
+  return kv8 && NRT == 1 && D <= 128 && !persistent ? 2 : 1;
+}
+
 // Largest batch the persistent schedule handles (its per-sequence prefix sums
 // live in shared memory); larger batches use the grid schedule.
 constexpr int kPsMaxBatch = 1024;
@@ -102,7 +115,7 @@ struct ChunkBlocks {
 // 16 * (4c + lg) + 8x .. +7, and Q^T is loaded in the same order (a
 // contraction may visit its index in any order, as long as both operands
 // agree).
-template <int D, int NRT, int NW, bool STREAM, bool KV8, bool Q8>
+template <int D, int NRT, int NW, bool STREAM, bool KV8, bool Q8, bool PS>
 __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L, int q, int qoff,
                                          const SeqView& sv, int j_first, int j_last, int slot,
                                          bool write_out, int r0 = 0) {
@@ -138,6 +151,9 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
   static_assert(!Q8 || KV8, "an FP8 query goes with an FP8 KV cache");
   // Q^T operand of one k-step: 8 bf16 values, or 8 E4M3 codes (FP8 query).
   using QOp = std::conditional_t<Q8, uint64_t, bf16x8>;
+  // V^T registers of one dim tile: 8 bf16 values, or 8 E4M3 codes.
+  using VReg = std::conditional_t<KV8, u32x2, u32x4>;
+  constexpr int CPS = chunks_per_step(D, NRT, KV8, PS);  // 32-position chunks per loop step
 
   // Per-row visible interval inside this partition, and Q^T operands.
   int tlo[NRT], thi[NRT];
@@ -209,11 +225,13 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
     }
   };
   // V^T columns: lane (ln, lg) holds dim 16*dt + ln, positions 8*lg .. +7.
+  // The registers hold the cache's own bytes (FP8: 8 codes per dim tile,
+  // converted only when PV takes them).
   // bf16: 8-slot group = a [D][8] tile, one 16-byte load; the 16 lanes of a
   // lane group read 256 contiguous bytes.  FP8: 16-slot group = a [D][16]
   // tile, the 8 bytes of half lg % 2 of the dim's row; lane groups 2j and
   // 2j+1 together read 256 contiguous bytes.
-  auto load_v = [&](int k, const ChunkBlocks& cb, u32x4 (&vr)[DT], bool dummy) {
+  auto load_v = [&](int k, const ChunkBlocks& cb, VReg (&vr)[DT], bool dummy) {
     const int cs = cb0 + k * kChunk;
     int p8 = cs + 8 * lg;
     if (p8 + 8 <= ps || p8 >= pe) p8 = max(cs, ps) & ~7;  // wholly outside: any valid group, zeroed later
@@ -223,10 +241,7 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
     if constexpr (KV8) {
       const uint8_t* vp = vb + (dummy ? 0 : ((p8 & bs_mask) >> 4) * (D * 16) + ln * 16 + (p8 & 8));
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const u32x2 w = ld_kv8<STREAM>(vp + (dummy ? 0 : 256 * dt));
-        vr[dt] = u32x4{w[0], w[1], 0u, 0u};
-      }
+      for (int dt = 0; dt < DT; ++dt) vr[dt] = ld_kv8<STREAM>(vp + (dummy ? 0 : 256 * dt));
     } else {
       const uint8_t* vp = vb + (dummy ? 0 : ((p8 & bs_mask) >> 3) * (D * 16) + ln * 16);
 #pragma unroll
@@ -265,58 +280,81 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
   }
   if constexpr (Q8) scale_log2 *= *a.q_scale;
 
-  // Software pipeline, one chunk deep: the next chunk's K rows are requested
+  // Software pipeline, one step deep: the next step's K rows are requested
   // as soon as QK has consumed the current ones, its V columns as soon as PV
-  // has; block ids run two chunks ahead through the scalar cache.  Loads are
-  // issued unconditionally (after its last chunk a wave issues one-line dummy
-  // loads) so that the wait counts are the same on every path.
-  int k = wave;
-  u32x4 kr[2][KL], vr[DT];
-  ChunkBlocks nb = {0, 0, 0};
-  if (k < nck) {
-    const ChunkBlocks cb = blocks_of(k);
-    load_k(k, cb, kr, false);
-    load_v(k, cb, vr, false);
-    nb = blocks_of(min(k + NW, nck - 1));
+  // has; block ids run two steps ahead through the scalar cache.  Loads are
+  // issued unconditionally (after its last step a wave issues one-line dummy
+  // loads, and so does a step's chunk past the run's end) so that the wait
+  // counts are the same on every path.  Wave w takes steps w, w + NW, ...;
+  // step t covers chunks CPS*t .. CPS*t + CPS - 1.
+  const int nst = (nck + CPS - 1) / CPS;
+  // (with one chunk per step every chunk of a step below nst is in the run)
+  auto step_blocks = [&](int t, ChunkBlocks (&cb)[CPS]) {
+#pragma unroll
+    for (int c = 0; c < CPS; ++c) cb[c] = blocks_of(CPS == 1 ? t : min(t * CPS + c, nck - 1));
+  };
+  auto beyond = [&](int t, int c) { return CPS > 1 && t * CPS + c >= nck; };
+  int t = wave;
+  u32x4 kr[CPS][2][KL];
+  VReg vr[CPS][DT];
+  ChunkBlocks nb[CPS];
+#pragma unroll
+  for (int c = 0; c < CPS; ++c) nb[c] = ChunkBlocks{0, 0, 0};
+  if (t < nst) {
+    ChunkBlocks cb[CPS];
+    step_blocks(t, cb);
+#pragma unroll
+    for (int c = 0; c < CPS; ++c) {
+      load_k(t * CPS + c, cb[c], kr[c], beyond(t, c));
+      load_v(t * CPS + c, cb[c], vr[c], beyond(t, c));
+    }
+    step_blocks(min(t + NW, nst - 1), nb);
   }
-  for (; k < nck; k += NW) {
-    const bool past = k + NW >= nck;  // no next chunk for this wave
-    const int kn = min(k + NW, nck - 1);
-    const int cs = cb0 + k * kChunk;
-    const int p8 = cs + 8 * lg;
-    bf16x8 pb[NRT];
+  for (; t < nst; t += NW) {
+    const bool past = t + NW >= nst;  // no next step for this wave
+    const int tn = min(t + NW, nst - 1);
+    bf16x8 pb[CPS][NRT];
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
-      f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+      // visible iff tlo <= pos <= thi, as one unsigned comparison (rows that
+      // see nothing have tlo = 2^31 - 1, thi = -1: no pos >= 0 passes)
+      const uint32_t span = (uint32_t)(thi[rt] - tlo[rt]);
+      float x[CPS][8];
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        if constexpr (Q8) {  // E4M3 x E4M3 products, fp32 accumulation
-          sa = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k_codes(kr, 0, s), (long)qf[rt][s], sa,
-                                                         0, 0, 0);
-          sb = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k_codes(kr, 1, s), (long)qf[rt][s], sb,
-                                                         0, 0, 0);
-        } else {
-          sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(kr, 0, s), qf[rt][s], sa, 0, 0, 0);
-          sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(kr, 1, s), qf[rt][s], sb, 0, 0, 0);
+      for (int c = 0; c < CPS; ++c) {
+        f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          if constexpr (Q8) {  // E4M3 x E4M3 products, fp32 accumulation
+            sa = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k_codes(kr[c], 0, s), (long)qf[rt][s],
+                                                           sa, 0, 0, 0);
+            sb = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)k_codes(kr[c], 1, s), (long)qf[rt][s],
+                                                           sb, 0, 0, 0);
+          } else {
+            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(kr[c], 0, s), qf[rt][s], sa, 0, 0, 0);
+            sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(kr[c], 1, s), qf[rt][s], sb, 0, 0, 0);
+          }
+        }
+        const int p8 = cb0 + (t * CPS + c) * kChunk + 8 * lg;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[c][e] = (uint32_t)(p8 + e - tlo[rt]) <= span ? sa[e] * scale_log2 : -INFINITY;
+          x[c][4 + e] = (uint32_t)(p8 + 4 + e - tlo[rt]) <= span ? sb[e] * scale_log2 : -INFINITY;
         }
       }
-      // visible iff tlo <= t <= thi, as one unsigned comparison (rows that
-      // see nothing have tlo = 2^31 - 1, thi = -1: no t >= 0 passes)
-      const uint32_t span = (uint32_t)(thi[rt] - tlo[rt]);
-      float x[8];
+      float mx;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[e] = (uint32_t)(p8 + e - tlo[rt]) <= span ? sa[e] * scale_log2 : -INFINITY;
-        x[4 + e] = (uint32_t)(p8 + 4 + e - tlo[rt]) <= span ? sb[e] * scale_log2 : -INFINITY;
+      for (int c = 0; c < CPS; ++c) {
+        const float mc = fmaxf(fmaxf(fmaxf(x[c][0], x[c][1]), fmaxf(x[c][2], x[c][3])),
+                               fmaxf(fmaxf(x[c][4], x[c][5]), fmaxf(x[c][6], x[c][7])));
+        mx = c == 0 ? mc : fmaxf(mx, mc);
       }
-      float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                       fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      // Lazy rescaling: the reference max of a row moves only when the chunk
+      // Lazy rescaling: the reference max of a row moves only when the step
       // max exceeds it by more than kRescaleLog2 (or it is still -inf), so
       // weights stay <= 2^kRescaleLog2 and the accumulators are rescaled on
-      // few chunks instead of every chunk.  Any reference gives the exact
+      // few steps instead of every step.  Any reference gives the exact
       // final result: (m, l, o) stay consistent with one another.
       const bool grow = mx > mrun[rt] + kRescaleLog2;
       if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -331,49 +369,83 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
       const float mref = (mrun[rt] == -INFINITY) ? 0.f : mrun[rt];
       float psum = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const __bf16 pe16 = (__bf16)__builtin_amdgcn_exp2f(x[e] - mref);
-        pb[rt][e] = pe16;
-        psum += (float)pe16;  // normalise by the weights PV actually applies
+      for (int c = 0; c < CPS; ++c) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const __bf16 pe16 = (__bf16)__builtin_amdgcn_exp2f(x[c][e] - mref);
+          pb[c][rt][e] = pe16;
+          psum += (float)pe16;  // normalise by the weights PV actually applies
+        }
       }
       lrun[rt] += psum;
     }
-    load_k(kn, nb, kr, past);
-    const ChunkBlocks nb2 = blocks_of(min(k + 2 * NW, nck - 1));
+#pragma unroll
+    for (int c = 0; c < CPS; ++c) load_k(tn * CPS + c, nb[c], kr[c], past || beyond(tn, c));
+    ChunkBlocks nb2[CPS];
+    step_blocks(min(t + 2 * NW, nst - 1), nb2);
     // Keep V-dependent work below this point: the V columns are the last
     // loads to arrive, and waiting for them earlier would serialise the
-    // next chunk's K requests behind them.
+    // next step's K requests behind them.
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (KV8) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        vr[dt] = __builtin_bit_cast(u32x4, e4m3x8_to_bf16(vr[dt][0], vr[dt][1]));
-    }
-    if (cs < ps || cs + kChunk > pe) {
-      // Edge chunk: zero V entries of positions outside [ps, pe) so that a
-      // zero weight never meets a stale, possibly NaN, value.
-      u32x4 keep;
+    for (int c = 0; c < CPS; ++c) {
+      const int cs = cb0 + (t * CPS + c) * kChunk;
+      const int p8 = cs + 8 * lg;
+      if (cs < ps || cs + kChunk > pe) {
+        // Edge chunk: zero V entries of positions outside [ps, pe) so that a
+        // zero weight never meets a stale, possibly NaN, value (an E4M3 code
+        // of 0 is +0).
+        if constexpr (KV8) {
+          u32x2 keep;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int t0 = p8 + 2 * w;
-        const uint32_t lo16 = (t0 >= ps && t0 < pe) ? 0x0000ffffu : 0u;
-        const uint32_t hi16 = (t0 + 1 >= ps && t0 + 1 < pe) ? 0xffff0000u : 0u;
-        keep[w] = lo16 | hi16;
+          for (int w = 0; w < 2; ++w) {
+            uint32_t m = 0u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int t0 = p8 + 4 * w + e;
+              m |= (t0 >= ps && t0 < pe) ? 0xffu << (8 * e) : 0u;
+            }
+            keep[w] = m;
+          }
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) vr[c][dt] &= keep;
+        } else {
+          u32x4 keep;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const int t0 = p8 + 2 * w;
+            const uint32_t lo16 = (t0 >= ps && t0 < pe) ? 0x0000ffffu : 0u;
+            const uint32_t hi16 = (t0 + 1 >= ps && t0 + 1 < pe) ? 0xffff0000u : 0u;
+            keep[w] = lo16 | hi16;
+          }
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) vr[c][dt] &= keep;
+        }
       }
+      if constexpr (KV8) {  // each dim tile converted just before its products
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) vr[dt] &= keep;
-    }
+        for (int dt = 0; dt < DT; ++dt) {
+          const bf16x8 vop = e4m3x8_to_bf16(vr[c][dt][0], vr[c][dt][1]);
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
+          for (int rt = 0; rt < NRT; ++rt)
+            o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb[c][rt], o[rt][dt], 0, 0, 0);
+        }
+      } else {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vr[dt]), pb[rt], o[rt][dt], 0, 0, 0);
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vr[c][dt]), pb[c][rt], o[rt][dt],
+                                                                0, 0, 0);
+      }
     }
     // Request the next V columns only after PV has read these registers
-    // (no second register copy of the chunk).
+    // (no second register copy of the step).
     __builtin_amdgcn_sched_barrier(0);
-    load_v(kn, nb, vr, past);
-    nb = nb2;
+#pragma unroll
+    for (int c = 0; c < CPS; ++c) load_v(tn * CPS + c, nb[c], vr[c], past || beyond(tn, c));
+#pragma unroll
+    for (int c = 0; c < CPS; ++c) nb[c] = nb2[c];
   }
 
 #pragma unroll
@@ -470,7 +542,7 @@ __global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
   const int r0 = it.rb * 16 * NRT;                // first packed row of this block
   if (r0 >= a.group * q) return;                 // no row of this sequence is in it
   const int qoff = wave_row_offset(a.query_lens, it.b);
-  mfma_run<D, NRT, NW, STREAM, KV8, Q8>(a, it.b, it.h, L, q, qoff, sv, it.j, it.j, it.j, sv.nparts == 1,
+  mfma_run<D, NRT, NW, STREAM, KV8, Q8, false>(a, it.b, it.h, L, q, qoff, sv, it.j, it.j, it.j, sv.nparts == 1,
                                     r0);
 }
 
@@ -566,7 +638,7 @@ __global__ __launch_bounds__(64 * NW) void part_mfma_ps(PartArgs a) {
     const long w_first = ((A + 1) * W + total - 1) / total - 1;
     const int slot = (int)((long)blockIdx.x - w_first);
     const bool whole = (j1 == 0 && j2 == np_b - 1);
-    mfma_run<D, NRT, NW, STREAM, KV8, Q8>(a, b, h, L, q, s_q[b], sv, j1, j2, slot, whole);
+    mfma_run<D, NRT, NW, STREAM, KV8, Q8, true>(a, b, h, L, q, s_q[b], sv, j1, j2, slot, whole);
     // (one-shot plans have no workspace: every unit is whole and no merge runs)
     if (j2 == np_b - 1 && tid == 0 && a.ws_runs != nullptr)
       a.ws_runs[(size_t)b * H + h] = whole ? 0 : slot + 1;
