@@ -317,6 +317,31 @@ def test_grid_plans_with_few_waves(lib):
     assert (p["waves"], p["persistent"]) == (2, 1)
 
 
+def test_grid_splits_sized_by_loads_in_flight(lib):
+    # One-tile grid splits size the grid for ~64 KB of K/V loads in flight
+    # per CU if every unit had the longest span: 4 waves per CU at head dim
+    # 128 in bf16 (one 16 KB chunk per wave), 4 over an FP8 cache too (two
+    # 8 KB chunks per wave step), 8 at head dim 64, 2 at head dim 256; with
+    # partitions rounded down to fill that many workgroups.
+    def plan(B, hq, hkv, D, L, kv=pa.KV_NATIVE, q=1):
+        d = pa.make_dims(batch=B, num_q_heads=hq, head_dim=D, max_query_len=q, max_seq_len=L,
+                         max_blocks_per_seq=L // 16 + 1, num_blocks=B * (L // 16 + 1),
+                         dtype=pa.BF16, kv_format=kv)
+        return pa.plan(d, 0, hkv, 16, num_cus=256)
+    long = plan(1, 8, 1, 128, 131072)                     # 256 workgroups x 4 waves
+    assert (long["part_size"], long["num_parts"], long["waves"], long["persistent"]) == (512, 257, 4, 0)
+    assert plan(4, 32, 8, 128, 32768)["part_size"] == 4096   # 32 units: 8 partitions each
+    assert plan(2, 16, 2, 128, 65536)["part_size"] == 1024   # 4 units: 64 partitions each
+    assert plan(4, 32, 8, 128, 32768, kv=pa.KV_FP8_E4M3)["part_size"] == 4096
+    assert plan(1, 8, 1, 128, 131072, kv=pa.KV_FP8_E4M3)["part_size"] == 512
+    assert plan(2, 64, 8, 64, 16384)["part_size"] == 512     # head dim 64: 2 workgroups per CU
+    assert plan(1, 16, 2, 256, 16384)["part_size"] == 128    # head dim 256: 2 waves per CU
+    assert plan(1, 8, 1, 128, 32768)["part_size"] == 256     # floor of 8 chunks
+    # two row tiles keep the ~8-workgroups-per-CU split
+    r32 = plan(8, 32, 1, 128, 16384)
+    assert (r32["row_tiles"], r32["part_size"]) == (2, 256)
+
+
 def test_fp8_query_format_rules(lib):
     w = workloads.WORKLOADS["gqa_fp8qkv"]
     d = dims_of(w, kv_format=pa.KV_FP8_E4M3, q_format=pa.Q_FP8_E4M3)
