@@ -17,9 +17,9 @@ What is computed, and where it comes from:
   attention; the visible range starts at max(0, end - w).  Multi-token
   queries are the trailing tokens of the context (aiter PR #2914 "Pa gluon
   swa mtp opt", summary: sliding-window MTP decode), causal among themselves.
-  GQA groups query heads by H_q // H_kv (executorch PR #18759, review of
-  ``sdpa_decode_splitk``: "GQA is handled natively via H_q // H_kv
-  grouping").
+  GQA maps query head h_q to KV head h_q // (H_q // H_kv) (executorch PR
+  #18759, review of ``sdpa_decode_splitk``: grouped-query attention handled
+  inside the kernel by integer division of the head index).
 * ``paged_attention.decode_split`` — the split-K / flash-decoding algorithm
   (executorch PR #18759, Copilot overview and review suggestion 5; aiter PR
   #2914, workspace buffers ``max_logits`` / ``exp_sums`` /

@@ -110,8 +110,7 @@ def gather_keys(k_cache, table_row, positions, h, block_size):
     grp, u = offs // 16, offs % 16
     half = (u // 4) % 2
     place = u % 4 + 4 * (u // 8)
-    tiles = k_cache[blocks, h, grp, half]                    # [n, D/8, 8 places, 8]
-    cols = tiles[np.arange(n), :, place, :]                  # [n, D/8, 8]
+    cols = k_cache[blocks, h, grp, half, :, place, :]        # [n, D/E columns, E]
     return cols.reshape(n, k_cache.shape[4] * k_cache.shape[6]).astype(np.float64)
 
 
@@ -121,8 +120,7 @@ def gather_values(v_cache, table_row, positions, h, block_size):
     g = v_cache.shape[-1]
     blocks = table_row[positions // block_size]
     offs = positions % block_size
-    slabs = v_cache[blocks, h]                       # [n, bs/g, D, g]
-    return slabs[np.arange(len(positions)), offs // g, :, offs % g].astype(np.float64)
+    return v_cache[blocks, h, offs // g, :, offs % g].astype(np.float64)   # [n, D]
 
 
 def decode(q, k_cache, v_cache, block_tables, seq_lens, query_lens,
@@ -174,8 +172,9 @@ def partial_state(s, V):
 
     Split-K decode (executorch PR #18759, Copilot overview; aiter PR #2914
     workspace ``max_logits`` / ``exp_sums`` / ``temporary_output``).  A
-    partition with no visible position contributes nothing (gllm #116: "a
-    warp left with no positions contributes nothing"): m = -inf, l = 0, o = 0.
+    partition holding no visible position adds zero weight to the merge
+    (gllm #116, "What changes", CUDA kernels: a split whose window leaves it
+    no positions is left out of the combine): m = -inf, l = 0, o = 0.
     """
     if s.size == 0:
         return -math.inf, 0.0, np.zeros(V.shape[1])
