@@ -14,11 +14,38 @@
 #include <string>
 
 #include "pa_common.h"
-#include "pa_mfma.h"
+#include "pa_launch.h"
 #include "pa_reduce.h"
 #include "pa_valu.h"
 
+namespace pa_host {
+
+// Resident workgroups of a kernel on the current device (workgroups per CU
+// cached per kernel; the kernels are the same code on every gfx950 device).
+int resident_wgs(const void* fn, int threads, int cus) {
+  static std::mutex lock;
+  static const void* keys[64];
+  static int per_cu_of[64];
+  std::lock_guard<std::mutex> guard(lock);
+  int i = 0;
+  for (; i < 64 && keys[i] != nullptr; ++i)
+    if (keys[i] == fn) return per_cu_of[i] * cus;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  if (i < 64) {
+    keys[i] = fn;
+    per_cu_of[i] = per_cu;
+  }
+  return per_cu * cus;
+}
+
+}  // namespace pa_host
+
 namespace {
+
+using pa_host::Launch;
+using pa_host::launch_part;
 
 thread_local std::string g_last_error;
 
@@ -293,104 +320,6 @@ pa_status device_cu_count(int* out) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-// Resident workgroups of a kernel on the current device (workgroups per CU
-// cached per kernel; the kernels are the same code on every gfx950 device).
-int resident_wgs(const void* fn, int threads, int cus) {
-  static std::mutex lock;
-  static const void* keys[64];
-  static int per_cu_of[64];
-  std::lock_guard<std::mutex> guard(lock);
-  int i = 0;
-  for (; i < 64 && keys[i] != nullptr; ++i)
-    if (keys[i] == fn) return per_cu_of[i] * cus;
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0) != hipSuccess || per_cu < 1)
-    per_cu = 1;
-  if (i < 64) {
-    keys[i] = fn;
-    per_cu_of[i] = per_cu;
-  }
-  return per_cu * cus;
-}
-
-// Stream of a call and the caller's timing events.  With events, the
-// partition kernel is launched through hipExtLaunchKernel, which stamps them
-// with that dispatch's own start and end (the interval a kernel trace
-// reports), not with the times the stream reached two separate markers.
-struct Launch {
-  hipStream_t s;
-  hipEvent_t begin, end;
-};
-
-template <typename K>
-void launch_part(K kernel, dim3 grid, dim3 block, const Launch& L, const pa::PartArgs& a) {
-  if (L.begin || L.end)
-    hipExtLaunchKernelGGL(kernel, grid, block, 0, L.s, L.begin, L.end, 0, a);
-  else
-    hipLaunchKernelGGL(kernel, grid, block, 0, L.s, a);
-}
-
-// Persistent workgroups per CU for one-tile kernels: each wave has one
-// 32-position chunk of K and V in flight, and ~64 KB in flight per CU is
-// what the HBM gather needs; more resident waves than that only contend
-// (measured on MI355X against a full resident set of 3 workgroups per CU:
-// the large-block MTP batch 343-350 -> 326 us at one bf16 workgroup per CU,
-// the GQA batch 89.6-90.1 -> 87.8-88.5 us; FP8 caches best at two).
-template <int D, int NRT, int NW, bool KV8>
-constexpr int ps_wgs_per_cu() {
-  constexpr int chunk_bytes = pa::kChunk * 2 * D * (KV8 ? 1 : 2) * pa::chunks_per_step(D, NRT, KV8, true);
-  return NRT == 1 ? (65536 / (NW * chunk_bytes) > 1 ? 65536 / (NW * chunk_bytes) : 1) : 1 << 20;
-}
-
-template <int D, int NRT, int NW, bool STREAM, bool KV8, bool Q8>
-void launch_mfma_inst(dim3 grid, bool persistent, int cus, const Launch& L, const pa::PartArgs& a) {
-  if (persistent) {
-    const void* fn = (const void*)pa::part_mfma_ps<D, NRT, NW, STREAM, KV8, Q8>;
-    const int64_t cap = (int64_t)ps_wgs_per_cu<D, NRT, NW, KV8>() * cus;
-    const dim3 pgrid((unsigned)std::min<int64_t>(resident_wgs(fn, 64 * NW, cus), cap));
-    launch_part(pa::part_mfma_ps<D, NRT, NW, STREAM, KV8, Q8>, pgrid, dim3(64 * NW), L, a);
-  } else {
-    launch_part(pa::part_mfma<D, NRT, NW, STREAM, KV8, Q8>, grid, dim3(64 * NW), L, a);
-  }
-}
-
-template <int D, bool STREAM, bool KV8, bool Q8>
-bool launch_mfma_shape(int nrt, int nw, dim3 grid, bool persistent, int cus, const Launch& L,
-                       const pa::PartArgs& a) {
-  if constexpr (D == 256) {  // one row tile (the plan never asks for more)
-    switch (nrt * 8 + nw) {
-      case 1 * 8 + 1: launch_mfma_inst<D, 1, 1, STREAM, KV8, Q8>(grid, persistent, cus, L, a); return true;
-      case 1 * 8 + 2: launch_mfma_inst<D, 1, 2, STREAM, KV8, Q8>(grid, persistent, cus, L, a); return true;
-      case 1 * 8 + 4: launch_mfma_inst<D, 1, 4, STREAM, KV8, Q8>(grid, persistent, cus, L, a); return true;
-      default: return false;
-    }
-  } else {
-  switch (nrt * 8 + nw) {
-    case 1 * 8 + 1: launch_mfma_inst<D, 1, 1, STREAM, KV8, Q8>(grid, persistent, cus, L, a); return true;
-    case 1 * 8 + 2: launch_mfma_inst<D, 1, 2, STREAM, KV8, Q8>(grid, persistent, cus, L, a); return true;
-    case 1 * 8 + 4: launch_mfma_inst<D, 1, 4, STREAM, KV8, Q8>(grid, persistent, cus, L, a); return true;
-    case 2 * 8 + 1: launch_mfma_inst<D, 2, 1, STREAM, KV8, Q8>(grid, persistent, cus, L, a); return true;
-    case 2 * 8 + 2: launch_mfma_inst<D, 2, 2, STREAM, KV8, Q8>(grid, persistent, cus, L, a); return true;
-    case 3 * 8 + 1: launch_mfma_inst<D, 3, 1, STREAM, KV8, Q8>(grid, persistent, cus, L, a); return true;
-    case 4 * 8 + 1: launch_mfma_inst<D, 4, 1, STREAM, KV8, Q8>(grid, persistent, cus, L, a); return true;
-    default: return false;
-  }
-  }
-}
-
-template <int D>
-bool launch_mfma(int nrt, int nw, dim3 grid, bool persistent, bool streaming, bool kv8, bool q8,
-                 int cus, const Launch& L, const pa::PartArgs& a) {
-  if (q8)
-    return streaming ? launch_mfma_shape<D, true, true, true>(nrt, nw, grid, persistent, cus, L, a)
-                     : launch_mfma_shape<D, false, true, true>(nrt, nw, grid, persistent, cus, L, a);
-  if (kv8)
-    return streaming ? launch_mfma_shape<D, true, true, false>(nrt, nw, grid, persistent, cus, L, a)
-                     : launch_mfma_shape<D, false, true, false>(nrt, nw, grid, persistent, cus, L, a);
-  return streaming ? launch_mfma_shape<D, true, false, false>(nrt, nw, grid, persistent, cus, L, a)
-                   : launch_mfma_shape<D, false, false, false>(nrt, nw, grid, persistent, cus, L, a);
-}
-
 pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, const int32_t* seq_lens, const int32_t* query_lens,
               float scale, int32_t window, int32_t hkv, int32_t bs, const pa_dims* d,
@@ -404,8 +333,8 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
     return fail(PA_ERR_INVALID_ARG, "out, q, k_cache and v_cache must be 16-byte aligned");
   if (!aligned(block_tables, 4) || !aligned(seq_lens, 4) || !aligned(query_lens, 4))
     return fail(PA_ERR_INVALID_ARG, "int32 arrays must be 4-byte aligned");
-  if (workspace && !aligned(workspace, 16))
-    return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (workspace && !aligned(workspace, 256))
+    return fail(PA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   const bool kv8 = d->kv_format == PA_KV_FP8_E4M3;
   if (kv8) {
     // aiter PR #2914 review: FP8 caches without their scales must be refused,
@@ -491,9 +420,9 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
   bool ok = true;
   if (p.path == PA_PATH_MFMA) {
     switch (d->head_dim) {
-      case 64: ok = launch_mfma<64>(nrt, p.waves, grid, p.persistent, p.streaming, kv8, q8, cus, L, a); break;
-      case 128: ok = launch_mfma<128>(nrt, p.waves, grid, p.persistent, p.streaming, kv8, q8, cus, L, a); break;
-      default: ok = launch_mfma<256>(nrt, p.waves, grid, p.persistent, p.streaming, kv8, q8, cus, L, a); break;
+      case 64: ok = pa_host::launch_mfma_64(nrt, p.waves, grid, p.persistent, p.streaming, kv8, q8, cus, L, a); break;
+      case 128: ok = pa_host::launch_mfma_128(nrt, p.waves, grid, p.persistent, p.streaming, kv8, q8, cus, L, a); break;
+      default: ok = pa_host::launch_mfma_256(nrt, p.waves, grid, p.persistent, p.streaming, kv8, q8, cus, L, a); break;
     }
   } else if (d->dtype == PA_F32) {
     launch_part(pa::part_valu<float>, grid, dim3(256), L, a);
