@@ -261,24 +261,28 @@ def _validate(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, num_
         raise PaError(ERR_INVALID_ARG, "block_tables [B, M], seq_lens [B], query_lens [B]")
 
 
+def _nbytes(t) -> int:
+    """Size in bytes of a tensor's storage as the library sees it."""
+    return int(t.numel()) * int(t.element_size())
+
+
 def decode(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, scale, window,
-           num_kv_heads, block_size, max_seq_len, max_query_len=None, workspace=None,
+           num_kv_heads, block_size, max_seq_len, max_query_len, workspace=None,
            stream=None, path=0, part_size=0, waves=0, event_begin=None, event_end=None,
            schedule=0, loads=0, k_scale=None, v_scale=None, q_scale=None):
     """Runs pa_decode_ex on torch tensors; returns ``out``.
 
     ``max_seq_len`` / ``max_query_len`` are host-known upper bounds of the
     device arrays ``seq_lens`` / ``query_lens`` (the library never reads
-    device memory from the host).  ``workspace`` (uint8 CUDA tensor) is
-    allocated when not given and needed.
+    device memory from the host); both are required, since the plan (rows
+    per KV head, workspace size, schedule) scales with ``max_query_len``.
+    ``workspace`` (CUDA tensor of any dtype, 256-byte aligned) is allocated
+    when not given and needed.
     """
     import torch
     _validate(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, num_kv_heads, block_size)
     if q.shape[0] == 0:
         return out          # no query token in the batch: nothing to compute, nothing to call
-    if max_query_len is None:
-        max_query_len = int(q.shape[0]) if block_tables.shape[0] else 1
-        max_query_len = max(1, min(max_query_len, int(max_seq_len)))
     dims = dims_for(q, k_cache, block_tables, max_query_len, max_seq_len)
     opts = make_options(path, part_size, waves, event_begin, event_end, schedule, loads,
                         k_scale, v_scale, q_scale)
@@ -287,7 +291,7 @@ def decode(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, scale, 
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_bytes = _nbytes(workspace) if workspace is not None else 0
     _check(load().pa_decode_ex(
         ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(q.data_ptr()),
         ctypes.c_void_p(k_cache.data_ptr()), ctypes.c_void_p(v_cache.data_ptr()),
@@ -357,7 +361,7 @@ class Prepared:
             ctypes.c_float(scale), int(window), int(num_kv_heads), int(block_size),
             ctypes.byref(self.dims),
             vp(workspace.data_ptr()) if workspace is not None else None,
-            workspace.numel() if workspace is not None else 0,
+            _nbytes(workspace) if workspace is not None else 0,
             _stream_handle(stream), ctypes.byref(self.opts))
         self._fn = load().pa_decode_ex
 

@@ -7,8 +7,8 @@
 //     M = max_j m_j,  w_j = 2^(m_j - M) * l_j  (0 when m_j = -inf),
 //     out = sum_j w_j o_j / sum_j w_j.
 // A partition in which the row sees nothing has m_j = -inf, l_j = 0, o_j = 0
-// and weight 0 (gllm #116: a split with no positions "contributes
-// nothing").  Partitions are summed in a fixed order: results are
+// and weight 0 (gllm #116, "What changes": a split that the window leaves
+// with no positions adds nothing to the combine).  Partitions are summed in a fixed order: results are
 // deterministic.
 #pragma once
 

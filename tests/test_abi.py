@@ -292,7 +292,7 @@ def test_binding_rejects_cpu_tensors():
     c = workloads.make_case("tiny_f32", device="cpu")
     with pytest.raises(pa.PaError):
         pa.decode(c.new_out(), c.q, c.k_cache, c.v_cache, c.block_tables, c.seq_lens,
-                  c.query_lens, c.scale, 0, 1, 16, max_seq_len=50)
+                  c.query_lens, c.scale, 0, 1, 16, max_seq_len=50, max_query_len=1)
 
 
 def test_grid_plans_with_few_waves(lib):
