@@ -100,3 +100,20 @@ def test_counter_scaling_uses_the_calibration_copies():
     assert rec["dispatches"] == 3
     with pytest.raises(SystemExit):
         bench.counter_bytes([(0, "pa::part_mfma<...>", 1.0)], "WRITE_SIZE")   # no copy
+
+
+def test_parity_sample_keeps_extremes():
+    """The sampled full-size parity cases always compare the longest and the
+    shortest sequence besides the seeded draw, and never fewer than asked."""
+    import numpy as np
+    from tests._gpu_util import sample_sequences
+    import workloads
+    for name in ("large_block_mtp_bf16", "gqa_bf16", "swa_mtp_bf16"):
+        w = workloads.WORKLOADS[name]
+        g = __import__("torch").Generator().manual_seed(w.seed)
+        lens, _ = workloads._lengths(w, g)
+        for n, seed in ((2, 5), (10, 5), (10, 6), (24, 5)):
+            s = sample_sequences(lens, n, seed)
+            assert int(np.argmax(lens)) in s and int(np.argmin(lens)) in s
+            assert len(s) >= min(n, len(lens)) and s == sorted(set(s))
+    assert sample_sequences([5, 6, 7], None, 0) == [0, 1, 2]

@@ -23,8 +23,9 @@ def _need_gpu():
         pytest.skip("needs a GPU")
 
 
-@pytest.mark.parametrize("args", [["--workload", "tiny_f32", "--window", "5"],
-                                  ["--workload", "swa_mtp_bf16", "--flush", "--no-cpu-baseline"]])
+@pytest.mark.parametrize("args", [["--workload", "tiny_f32", "--window", "5", "--no-side"],
+                                  ["--workload", "swa_mtp_bf16", "--flush", "--no-cpu-baseline",
+                                   "--no-side"]])
 def test_bench_line(args):
     say(f"[case] bench {' '.join(args)}")
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "4",
@@ -51,3 +52,6 @@ def test_bench_line(args):
         cb = res["cpu_baseline"]
         assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0
         assert cb["parity_max_abs"] < 1e-4          # fp32 workload: the fp32 bar
+        assert cb["cpu_model"] and "threads" in cb["sample"]
+    pc = res["per_call"]
+    assert pc["reps"] >= 50 and pc["p10"] <= pc["median"] <= pc["p90"]

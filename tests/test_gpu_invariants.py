@@ -188,18 +188,6 @@ def test_one_partition_equals_many(name, window):
     assert worst <= 2.0 ** -6, name
 
 
-@pytest.mark.parametrize("name,window", [("gqa_bf16", 0), ("long_splitk_bf16", 0)])
-def test_peaked_logits(name, window):
-    """Q scaled by 3 (logits ~ N(0, 9)): outputs of order 0.3-1, so the
-    tolerance bites harder than at N(0, 1)."""
-    w = workloads.WORKLOADS[name]
-    c = workloads.make_case(w, device="cuda", window=window, q_gain=3.0)
-    out = run_gpu(c)
-    seqs = list(range(min(w.batch, 8)))
-    exp, rows = oracle_out(c, seqs)
-    compare(out, exp, rows, BF16_TOL, f"{name} peaked")
-
-
 @pytest.mark.parametrize("sched", [pa.SCHED_GRID, pa.SCHED_PERSISTENT])
 def test_load_forms_agree_bit_for_bit(sched):
     """Non-temporal and cached KV loads fetch the same bytes into the same

@@ -14,7 +14,8 @@ import torch
 import decode_attention_pa_amd as pa
 import workloads
 from oracle import paged_attention as ref
-from tests._gpu_util import BF16_TOL, F32_TOL, compare, oracle_out, run_gpu, say
+from tests._gpu_util import (BF16_TOL, F32_TOL, compare, oracle_out, run_gpu,
+                             sample_sequences, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -231,8 +232,10 @@ def _check_spans(c, win):
     say(f"[spans] {w.name} w={win}: bit-exact")
 
 
+# (workload, window, sampled sequences or None for all).  Sampled workloads
+# always include their longest and shortest sequences besides the draw.
 FULL = [("gqa_bf16", 0, None), ("swa_mtp_bf16", 128, None), ("long_splitk_bf16", 0, None),
-        ("large_block_mtp_bf16", 4096, 24), ("large_block_mtp_bf16", 0, 2)]
+        ("large_block_mtp_bf16", 4096, 24), ("large_block_mtp_bf16", 0, 10)]
 
 
 @pytest.mark.parametrize("sched", [pa.SCHED_AUTO, pa.SCHED_GRID])
@@ -242,18 +245,29 @@ def test_full_workload(name, window, nsample, sched):
     say(f"[case] full {name} window={window} schedule={sched}")
     c = workloads.make_case(w, device="cuda", window=window)
     out = run_gpu(c, schedule=sched)
-    B = w.batch
-    if nsample is None:
-        seqs = list(range(B))
-    else:
-        lens = np.array(c.seq_lens_host)
-        r = np.random.default_rng(w.seed)
-        pick = set([int(lens.argmax()), int(lens.argmin())])
-        pick |= set(int(x) for x in r.choice(B, size=nsample, replace=False))
-        seqs = sorted(pick)[:max(nsample, 2)]
+    seqs = sample_sequences(c.seq_lens_host, nsample, w.seed)
+    lens = [c.seq_lens_host[b] for b in seqs]
+    say(f"[sample] {len(seqs)} sequences, lengths {min(lens)}..{max(lens)}")
     exp, rows = oracle_out(c, seqs)
     compare(out, exp, rows, BF16_TOL, f"{name} w={window} seqs={len(seqs)}")
     # rows not compared must still be finite and written
+    assert torch.isfinite(out.float()).all()
+
+
+@pytest.mark.parametrize("name,window,nsample", FULL)
+def test_full_workload_peaked(name, window, nsample):
+    """Every full-size workload with Q scaled by 3 (logits ~ N(0, 9)), in the
+    launch configuration the bench times: the outputs are then of order
+    0.3-1, so the max-abs bar bites at every context length, not only the
+    scale-free ones."""
+    w = workloads.WORKLOADS[name]
+    say(f"[case] full peaked {name} window={window}")
+    c = workloads.make_case(w, device="cuda", window=window, q_gain=3.0)
+    out = run_gpu(c)
+    seqs = sample_sequences(c.seq_lens_host, nsample, w.seed + 1)
+    exp, rows = oracle_out(c, seqs)
+    mx, _ = compare(out, exp, rows, BF16_TOL, f"{name} peaked w={window} seqs={len(seqs)}")
+    assert float(np.abs(exp).max()) >= 0.1, "peaked outputs should be O(0.1-1)"
     assert torch.isfinite(out.float()).all()
 
 

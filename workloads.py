@@ -140,11 +140,11 @@ WORKLOADS = {
                     "context U[2048, 8192], window 0"),
     "large_block_mtp_bf16": Workload(
         name="large_block_mtp_bf16", dtype="bf16", batch=128, num_q_heads=64,
-        num_kv_heads=8, head_dim=128, block_size=1024, query_len=2, windows=(4096, 0),
+        num_kv_heads=8, head_dim=128, block_size=1024, query_len=2, windows=(0, 4096),
         scale=1.0 / math.sqrt(128.0), seed=5, max_blocks_per_seq=64,
         max_seq_len=65536, len_range=(2048, 65536),
         description="large-block mixed-window MTP decode bf16: B=128, 64/8 heads, "
-                    "D=128, bs=1024, context U[2048, 65536], q_len 2, window 4096 / 0"),
+                    "D=128, bs=1024, context U[2048, 65536], q_len 2, window 0 / 4096"),
 }
 
 
