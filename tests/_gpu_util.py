@@ -3,6 +3,7 @@ compact host copy of exactly the blocks it needs (data movement only)."""
 
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -123,6 +124,11 @@ def compare(out_gpu, expect, rows, tol, label=""):
     rel_bar, rms_bar = REL_BARS[tol]
     say(f"[parity] {label}: max_abs={mx:.3e} max|ref|={scale:.3e} rel={rel:.3e} "
         f"rms_ratio={rms_ratio:.3e} tol={tol:g} rel_bar={rel_bar:g} rms_bar={rms_bar:g}")
+    log = os.environ.get("PA_PARITY_LOG")
+    if log:
+        with open(log, "a", encoding="utf-8") as f:
+            f.write(f"{label}\tmax_abs={mx:.3e}\tmax_ref={scale:.3e}\trel={rel:.3e}\t"
+                    f"rms_ratio={rms_ratio:.3e}\n")
     assert mx <= tol, f"{label}: max-abs {mx:.3e} > {tol:g}"
     assert rel <= rel_bar, f"{label}: max-abs / max|ref| {rel:.3e} > {rel_bar:g}"
     assert rms_ratio <= rms_bar, f"{label}: RMS error / RMS ref {rms_ratio:.3e} > {rms_bar:g}"
