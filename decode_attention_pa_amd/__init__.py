@@ -60,7 +60,8 @@ class Plan(ctypes.Structure):
                 ("num_parts", ctypes.c_int32), ("waves", ctypes.c_int32),
                 ("one_shot", ctypes.c_int32), ("persistent", ctypes.c_int32),
                 ("row_tiles", ctypes.c_int32), ("row_blocks", ctypes.c_int32),
-                ("streaming", ctypes.c_int32), ("workspace_bytes", ctypes.c_uint64)]
+                ("streaming", ctypes.c_int32), ("ps_grid", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_uint64)]
 
     def as_dict(self) -> dict:
         return {f: getattr(self, f) for f, _ in self._fields_}

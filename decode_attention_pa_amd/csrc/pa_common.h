@@ -109,10 +109,13 @@ struct PartArgs {
   const int32_t* block_tables; // [B, max_blocks_per_seq]
   const int32_t* seq_lens;     // [B]
   const int32_t* query_lens;   // [B]
-  float* ws_m;                 // [B, H_kv, NP, R] running max, log2 domain
-  float* ws_l;                 // [B, H_kv, NP, R] exp-sum
-  float* ws_o;                 // [B, H_kv, NP, R, D] normalised partial output
-  int* ws_runs;                // [B, H_kv] states per unit (persistent schedule only)
+  float* ws_m;                 // [S, R] running max, log2 domain, per state slot
+  float* ws_l;                 // [S, R] exp-sum
+  float* ws_o;                 // [S, R, D] normalised partial output (S state slots:
+                               // B * H_kv * NP on the grid schedule, persistent grid
+                               // + B * H_kv on the persistent one)
+  int* ws_runs;                // [B, H_kv, 2] run count and first state slot per unit
+                               // (persistent schedule only)
   float scale_log2;            // scale * log2(e)
   int window;
   int num_q_heads;
@@ -173,7 +176,8 @@ struct ReduceArgs {
   const float* ws_m;
   const float* ws_l;
   const float* ws_o;
-  const int* ws_runs;   // states per unit, or null: every partition holds one
+  const int* ws_runs;   // per unit (run count, first state slot), or null: every
+                        // partition of unit u holds state slot u * NP + j
   int window;
   int num_q_heads;
   int num_kv_heads;

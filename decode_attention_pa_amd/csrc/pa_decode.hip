@@ -130,6 +130,27 @@ pa_status check_shape(const pa_dims* d, int32_t window, int32_t num_kv_heads, in
   return PA_OK;
 }
 
+// Workspace of a split plan: state slots (each R rows) of max, exp-sum and
+// normalised output, 256-byte aligned regions; the persistent schedule adds
+// a (run count, first slot) pair per unit.  Slots: one per (unit, partition)
+// on the grid schedule, persistent grid + units on the persistent one.
+struct WsLayout {
+  uint64_t states;  // state rows (slots x R)
+  uint64_t off_l, off_o, off_runs, total;
+};
+
+WsLayout workspace_layout(const pa_plan& r, const pa_dims& d, int hkv) {
+  WsLayout w;
+  const uint64_t units = (uint64_t)d.batch * hkv;
+  const uint64_t slots = r.persistent ? (uint64_t)r.ps_grid + units : units * r.num_parts;
+  w.states = slots * r.rows;
+  w.off_l = align256(w.states * 4);
+  w.off_o = w.off_l + align256(w.states * 4);
+  w.off_runs = w.off_o + align256(w.states * d.head_dim * 4);
+  w.total = w.off_runs + (r.persistent ? align256(units * 8) : 0);
+  return w;
+}
+
 pa_status make_plan(const pa_dims* d, int32_t window, int32_t hkv, int32_t bs, int32_t num_cus,
                     const pa_options* o, pa_plan* p) {
   pa_status st = check_shape(d, window, hkv, bs);
@@ -290,12 +311,15 @@ pa_status make_plan(const pa_dims* d, int32_t window, int32_t hkv, int32_t bs, i
   }
   const bool reread = r.row_blocks > 1;
   r.streaming = r.path != PA_PATH_MFMA ? 0 : (loads_req == 2 ? 1 : (loads_req == 1 ? 0 : !reread));
+  r.ps_grid = 0;
+  if (r.persistent) {
+    const bool kv8 = d->kv_format == PA_KV_FP8_E4M3;
+    r.ps_grid = pa::ps_wgs_per_cu(d->head_dim, r.row_tiles, r.waves, kv8) * num_cus;
+  }
   if (r.one_shot) {
     r.workspace_bytes = 0;
   } else {
-    const uint64_t states = (uint64_t)d->batch * hkv * r.num_parts * r.rows;
-    r.workspace_bytes = 2 * align256(states * 4) + align256(states * d->head_dim * 4) +
-                        (r.persistent ? align256((uint64_t)d->batch * hkv * 4) : 0);
+    r.workspace_bytes = workspace_layout(r, *d, hkv).total;
   }
   *p = r;
   return PA_OK;
@@ -367,13 +391,13 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
     std::fprintf(stderr,
                  "[pa_decode] B=%d Hq=%d Hkv=%d D=%d bs=%d w=%d kv8=%d q8=%d R=%d span_max=%d path=%s "
                  "P=%d NP=%d waves=%d row_tiles=%d row_blocks=%d one_shot=%d persistent=%d "
-                 "streaming=%d ws=%llu cus=%d\n",
+                 "ps_grid=%d streaming=%d ws=%llu cus=%d\n",
                  d->batch, d->num_q_heads, hkv, d->head_dim, bs, window, (int)kv8, (int)q8, p.rows,
                  p.span_max, p.path == PA_PATH_MFMA ? "mfma" : "valu", p.part_size, p.num_parts,
-                 p.waves, p.row_tiles, p.row_blocks, p.one_shot, p.persistent, p.streaming,
+                 p.waves, p.row_tiles, p.row_blocks, p.one_shot, p.persistent, p.ps_grid, p.streaming,
                  (unsigned long long)p.workspace_bytes, cus);
 
-  const uint64_t states = (uint64_t)d->batch * hkv * p.num_parts * p.rows;
+  const WsLayout wl = workspace_layout(p, *d, hkv);
   char* ws = (char*)workspace;
   pa::PartArgs a = {};
   a.out = out;
@@ -384,11 +408,9 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
   a.seq_lens = seq_lens;
   a.query_lens = query_lens;
   a.ws_m = p.one_shot ? nullptr : (float*)ws;
-  a.ws_l = p.one_shot ? nullptr : (float*)(ws + align256(states * 4));
-  a.ws_o = p.one_shot ? nullptr : (float*)(ws + 2 * align256(states * 4));
-  a.ws_runs = (p.one_shot || !p.persistent)
-                  ? nullptr
-                  : (int*)(ws + 2 * align256(states * 4) + align256(states * d->head_dim * 4));
+  a.ws_l = p.one_shot ? nullptr : (float*)(ws + wl.off_l);
+  a.ws_o = p.one_shot ? nullptr : (float*)(ws + wl.off_o);
+  a.ws_runs = (p.one_shot || !p.persistent) ? nullptr : (int*)(ws + wl.off_runs);
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.window = window;
   a.num_q_heads = d->num_q_heads;
@@ -415,7 +437,9 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
                            ? (units + pa::kXcds - 1) / pa::kXcds * pa::kXcds * p.row_blocks
                            : units;
   if (nwg > 0x7fffffffull) return fail(PA_ERR_UNSUPPORTED, "grid of %llu workgroups too large", (unsigned long long)nwg);
-  const dim3 grid((uint32_t)nwg);
+  // persistent plans launch at most the plan's grid bound (the kernel caps
+  // it further at what fits on the device at once)
+  const dim3 grid(p.persistent ? (uint32_t)p.ps_grid : (uint32_t)nwg);
   const int nrt = p.row_tiles;
   bool ok = true;
   if (p.path == PA_PATH_MFMA) {
@@ -449,11 +473,11 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
     r.num_parts = p.num_parts;
     r.part_size = p.part_size;
     r.head_dim = d->head_dim;
-    // persistent: a unit has about one state per workgroup share it crosses;
-    // with ~4 resident workgroups per CU, balanced units cross about
-    // (resident workgroups / units) + 2 shares (a lone long unit crosses them all)
+    // persistent: a unit has one state per workgroup share it crosses;
+    // balanced units cross about (grid / units) + 2 shares (a lone long unit
+    // crosses them all)
     const int64_t bh = (int64_t)d->batch * hkv;
-    const int64_t ps_runs = (4 * (int64_t)cus + bh - 1) / bh + 2;
+    const int64_t ps_runs = ((int64_t)p.ps_grid + bh - 1) / bh + 2;
     const int gp = pa::reduce_group_lanes(
         p.persistent ? (int)std::min<int64_t>(p.num_parts, ps_runs) : p.num_parts);
     const int vec = d->head_dim % 4 == 0 ? 4 : 1;  // dims per merge unit

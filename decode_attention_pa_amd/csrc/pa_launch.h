@@ -35,24 +35,13 @@ void launch_part(K kernel, dim3 grid, dim3 block, const Launch& L, const pa::Par
     hipLaunchKernelGGL(kernel, grid, block, 0, L.s, a);
 }
 
-// Persistent workgroups per CU for one-tile kernels: each wave has one
-// 32-position chunk of K and V in flight, and ~64 KB in flight per CU is
-// what the HBM gather needs; more resident waves than that only contend
-// (measured on MI355X against a full resident set of 3 workgroups per CU:
-// the large-block MTP batch 343-350 -> 326 us at one bf16 workgroup per CU,
-// the GQA batch 89.6-90.1 -> 87.8-88.5 us; FP8 caches best at two).
-template <int D, int NRT, int NW, bool KV8>
-constexpr int ps_wgs_per_cu() {
-  constexpr int chunk_bytes = pa::kChunk * 2 * D * (KV8 ? 1 : 2) * pa::chunks_per_step(D, NRT, KV8, true);
-  return NRT == 1 ? (65536 / (NW * chunk_bytes) > 1 ? 65536 / (NW * chunk_bytes) : 1) : 1 << 20;
-}
-
 template <int D, int NRT, int NW, bool STREAM, bool KV8, bool Q8>
 void launch_mfma_inst(dim3 grid, bool persistent, int cus, const Launch& L, const pa::PartArgs& a) {
   if (persistent) {
+    // grid.x: the plan's bound on the persistent grid (it sized the
+    // workspace for that many workgroups); never more than fit at once
     const void* fn = (const void*)pa::part_mfma_ps<D, NRT, NW, STREAM, KV8, Q8>;
-    const int64_t cap = (int64_t)ps_wgs_per_cu<D, NRT, NW, KV8>() * cus;
-    const dim3 pgrid((unsigned)std::min<int64_t>(resident_wgs(fn, 64 * NW, cus), cap));
+    const dim3 pgrid((unsigned)std::min<int64_t>(resident_wgs(fn, 64 * NW, cus), (int64_t)grid.x));
     launch_part(pa::part_mfma_ps<D, NRT, NW, STREAM, KV8, Q8>, pgrid, dim3(64 * NW), L, a);
   } else {
     launch_part(pa::part_mfma<D, NRT, NW, STREAM, KV8, Q8>, grid, dim3(64 * NW), L, a);

@@ -93,6 +93,21 @@ constexpr int chunks_per_step(int D, int NRT, bool kv8, bool persistent) {
   return kv8 && NRT == 1 && D <= 128 && !persistent ? 2 : 1;
 }
 
+// Resident workgroups per CU the persistent schedule launches (it caps the
+// hardware's resident count at this).  One-tile kernels: each wave has one
+// 32-position chunk of K and V in flight, and ~64 KB in flight per CU is
+// what the HBM gather needs; more resident waves than that only contend
+// (measured on MI355X against a full resident set of 3 workgroups per CU:
+// the large-block MTP batch 343-350 -> 326 us at one bf16 workgroup per CU,
+// the GQA batch 89.6-90.1 -> 87.8-88.5 us; FP8 caches best at two).
+// Several row tiles: whatever fits, bounded by 16 waves per CU.  The plan
+// sizes the workspace from the same bound.
+__host__ __device__ constexpr int ps_wgs_per_cu(int D, int NRT, int NW, bool kv8) {
+  return NRT == 1 ? (65536 / (NW * kChunk * 2 * D * (kv8 ? 1 : 2)) > 1
+                         ? 65536 / (NW * kChunk * 2 * D * (kv8 ? 1 : 2)) : 1)
+                  : (16 / NW > 1 ? 16 / NW : 1);
+}
+
 // Largest batch the persistent schedule handles (its per-sequence prefix sums
 // live in shared memory); larger batches use the grid schedule.
 constexpr int kPsMaxBatch = 1024;
@@ -106,8 +121,8 @@ struct ChunkBlocks {
 // One run: partitions j_first .. j_last of unit (sequence b, KV head h),
 // processed as one stretch of positions by the NW waves of the workgroup.
 // With `write_out` (the run is the whole unit) it writes `out`; otherwise its
-// state (max, exp-sum, normalised output) goes to workspace slot `slot` of
-// the unit.  All waves of the workgroup call this with the same arguments.
+// state (max, exp-sum, normalised output) goes to workspace state slot
+// `state` (R rows per slot).  All waves of the workgroup call this with the same arguments.
 // KV8: K and V hold OCP E4M3 codes (16 per 16-byte column / V row) that are
 // converted to bf16 in registers; the K scale folds into the logit scale and
 // the V scale into the output normalisation.  With 16 dims per K column, one
@@ -117,7 +132,7 @@ struct ChunkBlocks {
 // agree).
 template <int D, int NRT, int NW, bool STREAM, bool KV8, bool Q8, bool PS>
 __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L, int q, int qoff,
-                                         const SeqView& sv, int j_first, int j_last, int slot,
+                                         const SeqView& sv, int j_first, int j_last, size_t state,
                                          bool write_out, int r0 = 0) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
@@ -518,7 +533,7 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
           *(bf16x4*)(op + 16 * dt + 4 * lg) = v;
         }
       } else {
-        const size_t w = (((size_t)b * a.num_kv_heads + h) * a.num_parts + slot) * a.rows + n;
+        const size_t w = state * a.rows + n;
         if (lg == 0) {
           a.ws_m[w] = mrun[rt];
           a.ws_l[w] = lrun[rt];
@@ -542,8 +557,9 @@ __global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
   const int r0 = it.rb * 16 * NRT;                // first packed row of this block
   if (r0 >= a.group * q) return;                 // no row of this sequence is in it
   const int qoff = wave_row_offset(a.query_lens, it.b);
-  mfma_run<D, NRT, NW, STREAM, KV8, Q8, false>(a, it.b, it.h, L, q, qoff, sv, it.j, it.j, it.j, sv.nparts == 1,
-                                    r0);
+  const size_t state = ((size_t)it.b * a.num_kv_heads + it.h) * a.num_parts + it.j;
+  mfma_run<D, NRT, NW, STREAM, KV8, Q8, false>(a, it.b, it.h, L, q, qoff, sv, it.j, it.j, state,
+                                               sv.nparts == 1, r0);
 }
 
 // Persistent schedule (aiter PR #2914: "PS" decode): a grid whose
@@ -554,9 +570,13 @@ __global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
 // unit's stretch of it as one run.  Shares differ by at most one partition,
 // so there is no tail of late workgroups, and a workgroup's set-up is paid
 // once per unit it touches rather than once per partition.  A run that is a
-// whole unit writes `out`; otherwise it stores its state in slot k = its
-// ordinal among the unit's runs, and the unit's last run records the number
-// of states for the merge (0 when the unit was written directly).
+// whole unit writes `out`; otherwise it stores its state in slot w + u (w
+// its workgroup, u = b * H_kv + h its unit).  Walking the shares in order,
+// each (share, unit) pair steps w, u or both up by one, so these slots are
+// distinct, those of one unit are consecutive (w_first + u onwards), and
+// all lie below W + units: the workspace holds W + units states, whatever
+// the partition count.  The unit's last run records its run count and first
+// slot for the merge (count 0 when the unit was written directly).
 template <int D, int NRT, int NW, bool STREAM, bool KV8, bool Q8>
 __global__ __launch_bounds__(64 * NW) void part_mfma_ps(PartArgs a) {
   constexpr int NT = 64 * NW;
@@ -638,10 +658,12 @@ __global__ __launch_bounds__(64 * NW) void part_mfma_ps(PartArgs a) {
     const long w_first = ((A + 1) * W + total - 1) / total - 1;
     const int slot = (int)((long)blockIdx.x - w_first);
     const bool whole = (j1 == 0 && j2 == np_b - 1);
-    mfma_run<D, NRT, NW, STREAM, KV8, Q8, true>(a, b, h, L, q, s_q[b], sv, j1, j2, slot, whole);
+    const size_t unit = (size_t)b * H + h;
+    mfma_run<D, NRT, NW, STREAM, KV8, Q8, true>(a, b, h, L, q, s_q[b], sv, j1, j2,
+                                              (size_t)blockIdx.x + unit, whole);
     // (one-shot plans have no workspace: every unit is whole and no merge runs)
     if (j2 == np_b - 1 && tid == 0 && a.ws_runs != nullptr)
-      a.ws_runs[(size_t)b * H + h] = whole ? 0 : slot + 1;
+      *(int2*)(a.ws_runs + 2 * unit) = make_int2(whole ? 0 : slot + 1, (int)(w_first + (long)unit));
     __syncthreads();  // the next run reuses the merge's shared memory
     i0 += j2 - j1 + 1;
   }

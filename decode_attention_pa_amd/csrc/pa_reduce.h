@@ -65,12 +65,14 @@ __global__ __launch_bounds__(256) void lse_reduce(ReduceArgs a) {
   // One round of independent loads: lengths, run count, row offset.
   const int L = a.seq_lens[b];
   const int q = a.query_lens[b];
-  const int runs = a.ws_runs ? a.ws_runs[(size_t)b * a.num_kv_heads + h] : 0;
+  // persistent schedule: the unit's run count and first state slot
+  const int2 rs = a.ws_runs ? *(const int2*)(a.ws_runs + 2 * ((size_t)b * a.num_kv_heads + h))
+                            : make_int2(0, 0);
   const int qoff = wave_row_offset(a.query_lens, b);  // all lanes still active
   const int G = a.group;
   const SeqView sv = seq_view(L, q, a.window, a.part_size);
   // states to merge: one per partition, or the unit's run count
-  const int np = a.ws_runs ? min(runs, a.num_parts) : (sv.nparts > 1 ? min(sv.nparts, a.num_parts) : 0);
+  const int np = a.ws_runs ? rs.x : (sv.nparts > 1 ? min(sv.nparts, a.num_parts) : 0);
   if (np <= 0) return;  // the partition kernel wrote these rows directly (whole workgroup)
   const int unit = blockIdx.x * UPW + tid % UPW;
   const int gp = tid / UPW;
@@ -79,7 +81,9 @@ __global__ __launch_bounds__(256) void lse_reduce(ReduceArgs a) {
   // the workgroup.  With GP = 1 there is no combine and they leave now.
   const bool live = n < G * q;
   if (GP == 1 && !live) return;
-  const size_t base = ((size_t)b * a.num_kv_heads + h) * a.num_parts;
+  // first state slot of the unit: partition j of a grid plan sits at slot
+  // unit * NP + j; the persistent runs of a unit at consecutive slots
+  const size_t base = a.ws_runs ? (size_t)rs.y : ((size_t)b * a.num_kv_heads + h) * a.num_parts;
 
   // One pass: each thread keeps a running reference max mt over its own
   // partitions (rescaling its sums when it grows), then the group agrees on

@@ -153,7 +153,13 @@ typedef struct pa_plan {
                                  workgroup); 0: cached loads (row blocks share K/V through
                                  L2, or forced).  Matrix-core path only (0 on the vector
                                  path) */
-  uint64_t workspace_bytes;   /* bytes pa_decode needs in `workspace` (0 if one_shot) */
+  int32_t ps_grid;            /* persistent schedule: most workgroups its grid may hold
+                                 (fewer when fewer fit on the device at once); 0 otherwise */
+  uint64_t workspace_bytes;   /* bytes pa_decode needs in `workspace` (0 if one_shot):
+                                 partial states of B*H_kv*num_parts slots on the grid
+                                 schedule, of ps_grid + B*H_kv slots on the persistent one
+                                 (R rows of D + 2 floats each), plus 8 bytes per
+                                 (sequence, KV head) on the persistent schedule */
 } pa_plan;
 
 /* Optional controls for pa_decode_ex / pa_plan_compute (zero = automatic). */

@@ -76,10 +76,13 @@ def test_plan_covers_longest_span(lib, name):
         if p["one_shot"]:
             assert p["workspace_bytes"] == 0
         else:
-            states = w.batch * w.num_kv_heads * p["num_parts"] * p["rows"]
+            units = w.batch * w.num_kv_heads
+            slots = p["ps_grid"] + units if p["persistent"] else units * p["num_parts"]
+            states = slots * p["rows"]
             al = lambda x: (x + 255) // 256 * 256
-            runs = al(4 * w.batch * w.num_kv_heads) if p["persistent"] else 0
+            runs = al(8 * units) if p["persistent"] else 0
             assert p["workspace_bytes"] == 2 * al(4 * states) + al(4 * states * w.head_dim) + runs
+            assert p["ps_grid"] > 0 if p["persistent"] else p["ps_grid"] == 0
         expect_path = pa.PATH_VALU if w.dtype == "f32" else pa.PATH_MFMA
         assert p["path"] == expect_path
 
