@@ -35,8 +35,8 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 
 EXPORTED_SYMBOLS = (
     "pa_plan_compute", "pa_decode_workspace_size", "pa_decode_workspace_size_ex",
-    "pa_decode", "pa_decode_ex", "pa_debug_spans", "pa_check_inputs", "pa_status_string",
-    "pa_last_error",
+    "pa_decode", "pa_decode_ex", "pa_decode_noalloc", "pa_noalloc_scratch_bytes",
+    "pa_debug_spans", "pa_check_inputs", "pa_status_string", "pa_last_error",
 )
 
 
@@ -102,6 +102,9 @@ def load() -> ctypes.CDLL:
     lib.pa_decode.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, I32, I32, I32, pd, P,
                               ctypes.c_size_t, P]
     lib.pa_decode_ex.argtypes = lib.pa_decode.argtypes + [po]
+    lib.pa_decode_noalloc.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, I32, I32, I32, pd, P, po]
+    lib.pa_noalloc_scratch_bytes.argtypes = []
+    lib.pa_noalloc_scratch_bytes.restype = ctypes.c_size_t
     lib.pa_debug_spans.argtypes = [P, P, P, I32, I32, I32, pd, po, P, P, P, P, P]
     lib.pa_check_inputs.argtypes = [P, P, P, I32, I32, I32, pd, P, P]
     lib.pa_status_string.argtypes = [I32]
@@ -109,7 +112,8 @@ def load() -> ctypes.CDLL:
     lib.pa_last_error.argtypes = []
     lib.pa_last_error.restype = ctypes.c_char_p
     for name in ("pa_plan_compute", "pa_decode_workspace_size", "pa_decode_workspace_size_ex",
-                 "pa_decode", "pa_decode_ex", "pa_debug_spans", "pa_check_inputs"):
+                 "pa_decode", "pa_decode_ex", "pa_decode_noalloc", "pa_debug_spans",
+                 "pa_check_inputs"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -301,6 +305,33 @@ def decode(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, scale, 
         int(num_kv_heads), int(block_size), ctypes.byref(dims), ws_ptr, ws_bytes,
         _stream_handle(stream), ctypes.byref(opts)))
     return out
+
+
+def decode_noalloc(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, scale, window,
+                   num_kv_heads, block_size, max_seq_len, max_query_len, stream=None, path=0,
+                   part_size=0, waves=0, schedule=0, loads=0, k_scale=None, v_scale=None,
+                   q_scale=None):
+    """Runs pa_decode_noalloc on torch tensors (no workspace: the library's
+    static per-GPU scratch holds the partial states); returns ``out``."""
+    _validate(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, num_kv_heads, block_size)
+    if q.shape[0] == 0:
+        return out          # no query token in the batch: nothing to compute, nothing to call
+    dims = dims_for(q, k_cache, block_tables, max_query_len, max_seq_len)
+    opts = make_options(path, part_size, waves, None, None, schedule, loads, k_scale, v_scale,
+                        q_scale)
+    _check(load().pa_decode_noalloc(
+        ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(q.data_ptr()),
+        ctypes.c_void_p(k_cache.data_ptr()), ctypes.c_void_p(v_cache.data_ptr()),
+        ctypes.c_void_p(block_tables.data_ptr()), ctypes.c_void_p(seq_lens.data_ptr()),
+        ctypes.c_void_p(query_lens.data_ptr()), ctypes.c_float(scale), int(window),
+        int(num_kv_heads), int(block_size), ctypes.byref(dims), _stream_handle(stream),
+        ctypes.byref(opts)))
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    """Size of the static scratch pa_decode_noalloc uses on each GPU."""
+    return int(load().pa_noalloc_scratch_bytes())
 
 
 def debug_spans(block_tables, seq_lens, query_lens, window, num_kv_heads, block_size, dims: Dims,

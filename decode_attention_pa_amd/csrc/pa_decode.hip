@@ -501,6 +501,40 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
   return PA_OK;
 }
 
+// Workspace of pa_decode_noalloc: a fixed device array instead of
+// caller-owned memory, for callers that cannot allocate.  Each GPU the
+// library runs on holds its own copy until the process ends; in host code
+// the array's name is only a stand-in, so its device address is looked up
+// once per device (with that device current) and kept.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_lock;
+void* g_scratch_ptr[64];
+
+// Device address of `scratch` on the current device.
+pa_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(PA_ERR_HIP, "device ordinal %d out of range", dev);
+  std::lock_guard<std::mutex> guard(g_scratch_lock);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr || !aligned(ptr, 256)) return fail(PA_ERR_HIP, "scratch address %p unusable", ptr);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -549,6 +583,36 @@ pa_status pa_decode_ex(void* out, const void* q, const void* k_cache, const void
   return run(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, scale, window,
              num_kv_heads, block_size, dims, workspace, workspace_bytes, hip_stream, opts);
 }
+
+pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* seq_lens,
+                            const int32_t* query_lens, float scale, int32_t window,
+                            int32_t num_kv_heads, int32_t block_size, const pa_dims* dims,
+                            void* hip_stream, const pa_options* opts) {
+  pa_status st = check_shape(dims, window, num_kv_heads, block_size);
+  if (st != PA_OK) return st;
+  if (dims->batch == 0) return PA_OK;
+  int cus = 0;
+  st = device_cu_count(&cus);
+  if (st != PA_OK) return st;
+  pa_plan p;
+  st = make_plan(dims, window, num_kv_heads, block_size, cus, opts, &p);
+  if (st != PA_OK) return st;
+  if (p.workspace_bytes > kScratchBytes)
+    return fail(PA_ERR_WORKSPACE,
+                "this plan needs %llu bytes of workspace, more than the %zu-byte static scratch "
+                "of pa_decode_noalloc; call pa_decode with a workspace instead",
+                (unsigned long long)p.workspace_bytes, kScratchBytes);
+  void* ws = nullptr;
+  if (p.workspace_bytes) {
+    st = scratch_address(&ws);
+    if (st != PA_OK) return st;
+  }
+  return run(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, scale, window,
+             num_kv_heads, block_size, dims, ws, ws ? kScratchBytes : 0, hip_stream, opts);
+}
+
+size_t pa_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 pa_status pa_debug_spans(const int32_t* block_tables, const int32_t* seq_lens,
                          const int32_t* query_lens, int32_t window, int32_t num_kv_heads,

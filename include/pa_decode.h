@@ -234,6 +234,29 @@ pa_status pa_decode_ex(void* out, const void* q, const void* k_cache, const void
                        const pa_options* opts);
 
 /*
+ * pa_decode_ex without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The partial states live in a static
+ * device array of pa_noalloc_scratch_bytes() bytes (64 MiB) that each GPU
+ * the library runs on holds until the process ends; no call allocates or
+ * frees anything.  A plan whose workspace (pa_decode_workspace_size_ex)
+ * exceeds it returns PA_ERR_WORKSPACE before any launch.  Nothing in the
+ * scratch has to start at zero: every byte a call reads was written by the
+ * same call.  All calls on one GPU share the array, so calls that may
+ * overlap on one GPU (different streams, other threads, other processes'
+ * copies excepted) race and must be ordered by the caller, e.g. on one
+ * stream.  Other arguments and errors as pa_decode_ex.
+ */
+pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* seq_lens,
+                            const int32_t* query_lens, float scale, int32_t window,
+                            int32_t num_kv_heads, int32_t block_size, const pa_dims* dims,
+                            void* hip_stream, const pa_options* opts);
+
+/* Size in bytes of pa_decode_noalloc's static scratch. */
+size_t pa_noalloc_scratch_bytes(void);
+
+/*
  * Index dump for bit-exact checks: runs the device index helpers the
  * partition kernels use and writes, into device int32 arrays,
  *   seq_info  [B, 4]   qoff_b, lo_b, hi_b (union of visible ranges [lo_b, hi_b)),
