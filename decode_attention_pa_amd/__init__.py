@@ -36,7 +36,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 EXPORTED_SYMBOLS = (
     "pa_plan_compute", "pa_decode_workspace_size", "pa_decode_workspace_size_ex",
     "pa_decode", "pa_decode_ex", "pa_decode_noalloc", "pa_noalloc_scratch_bytes",
-    "pa_debug_spans", "pa_check_inputs", "pa_status_string", "pa_last_error",
+    "pa_pack_kv_cache", "pa_debug_spans", "pa_check_inputs", "pa_status_string", "pa_last_error",
 )
 
 
@@ -103,6 +103,7 @@ def load() -> ctypes.CDLL:
                               ctypes.c_size_t, P]
     lib.pa_decode_ex.argtypes = lib.pa_decode.argtypes + [po]
     lib.pa_decode_noalloc.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, I32, I32, I32, pd, P, po]
+    lib.pa_pack_kv_cache.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, P]
     lib.pa_noalloc_scratch_bytes.argtypes = []
     lib.pa_noalloc_scratch_bytes.restype = ctypes.c_size_t
     lib.pa_debug_spans.argtypes = [P, P, P, I32, I32, I32, pd, po, P, P, P, P, P]
@@ -112,8 +113,8 @@ def load() -> ctypes.CDLL:
     lib.pa_last_error.argtypes = []
     lib.pa_last_error.restype = ctypes.c_char_p
     for name in ("pa_plan_compute", "pa_decode_workspace_size", "pa_decode_workspace_size_ex",
-                 "pa_decode", "pa_decode_ex", "pa_decode_noalloc", "pa_debug_spans",
-                 "pa_check_inputs"):
+                 "pa_decode", "pa_decode_ex", "pa_decode_noalloc", "pa_pack_kv_cache",
+                 "pa_debug_spans", "pa_check_inputs"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -327,6 +328,42 @@ def decode_noalloc(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens,
         int(num_kv_heads), int(block_size), ctypes.byref(dims), _stream_handle(stream),
         ctypes.byref(opts)))
     return out
+
+
+def pack_kv_cache(k_rows, v_rows, k_cache=None, v_cache=None, block_ids=None, stream=None):
+    """Repacks row-layout caches [num_blocks, H_kv, block_size, D] (float32,
+    bfloat16 or float8_e4m3fn) into the library's tiled layouts with
+    pa_pack_kv_cache; returns (k_cache, v_cache).  Without destination
+    tensors they are allocated; with ``block_ids`` (int32 CUDA tensor) only
+    those blocks are repacked into the given destinations."""
+    import torch
+    for name, t in (("k_rows", k_rows), ("v_rows", v_rows)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous() \
+                or t.dim() != 4:
+            raise PaError(ERR_INVALID_ARG, f"{name} must be a contiguous 4-d CUDA tensor")
+    if k_rows.shape != v_rows.shape or k_rows.dtype != v_rows.dtype:
+        raise PaError(ERR_INVALID_ARG, "k_rows and v_rows must share shape and dtype")
+    nb, hkv, bs, D = k_rows.shape
+    fp8 = k_rows.dtype == torch.float8_e4m3fn
+    dtype = BF16 if fp8 else _dtype_code(k_rows)
+    E = 16 if fp8 else 8
+    if k_cache is None:
+        kshape = (nb, hkv, bs // 16, 2, D // E, 8, E) if D % E == 0 else (nb, hkv, bs, D)
+        k_cache = torch.empty(kshape, dtype=k_rows.dtype, device=k_rows.device)
+    if v_cache is None:
+        v_cache = torch.empty((nb, hkv, bs // E, D, E), dtype=k_rows.dtype, device=k_rows.device)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.numel() != k_rows.numel() or t.dtype != k_rows.dtype or not t.is_contiguous():
+            raise PaError(ERR_INVALID_ARG, f"{name} must match k_rows in size and dtype")
+    if block_ids is not None and (block_ids.dtype != torch.int32 or block_ids.device.type != "cuda"):
+        raise PaError(ERR_INVALID_ARG, "block_ids must be an int32 CUDA tensor")
+    _check(load().pa_pack_kv_cache(
+        ctypes.c_void_p(k_rows.data_ptr()), ctypes.c_void_p(v_rows.data_ptr()),
+        ctypes.c_void_p(k_cache.data_ptr()), ctypes.c_void_p(v_cache.data_ptr()),
+        ctypes.c_void_p(block_ids.data_ptr()) if block_ids is not None else None,
+        int(block_ids.numel()) if block_ids is not None else 0, int(nb), int(hkv), int(bs), int(D),
+        int(dtype), KV_FP8_E4M3 if fp8 else KV_NATIVE, _stream_handle(stream)))
+    return k_cache, v_cache
 
 
 def noalloc_scratch_bytes() -> int:

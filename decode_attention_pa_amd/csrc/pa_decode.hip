@@ -15,6 +15,7 @@
 
 #include "pa_common.h"
 #include "pa_launch.h"
+#include "pa_pack.h"
 #include "pa_reduce.h"
 #include "pa_valu.h"
 
@@ -613,6 +614,56 @@ pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const
 }
 
 size_t pa_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+pa_status pa_pack_kv_cache(const void* k_rows, const void* v_rows, void* k_cache, void* v_cache,
+                           const int32_t* block_ids, int32_t num_ids, int32_t num_blocks,
+                           int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                           int32_t dtype, int32_t kv_format, void* hip_stream) {
+  if (!k_rows || !v_rows || !k_cache || !v_cache)
+    return fail(PA_ERR_INVALID_ARG, "a cache pointer is NULL");
+  if (!aligned(k_rows, 16) || !aligned(v_rows, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return fail(PA_ERR_INVALID_ARG, "cache pointers must be 16-byte aligned");
+  if (block_ids && !aligned(block_ids, 4)) return fail(PA_ERR_INVALID_ARG, "block_ids must be 4-byte aligned");
+  if (dtype != PA_F32 && dtype != PA_BF16)
+    return fail(PA_ERR_INVALID_ARG, "dtype %d is neither PA_F32 nor PA_BF16", dtype);
+  if (kv_format != PA_KV_NATIVE && kv_format != PA_KV_FP8_E4M3)
+    return fail(PA_ERR_INVALID_ARG, "kv_format %d unknown", kv_format);
+  if (num_blocks < 1) return fail(PA_ERR_INVALID_ARG, "num_blocks %d < 1", num_blocks);
+  if (num_kv_heads < 1 || num_kv_heads > 65535)
+    return fail(PA_ERR_INVALID_ARG, "num_kv_heads %d outside [1, 65535]", num_kv_heads);
+  if (ilog2_exact(block_size) < 4 || block_size > 1024)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d must be a power of two in [16, 1024]", block_size);
+  if (head_dim < 1 || head_dim > pa::kValuMaxD)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d outside [1, %d]", head_dim, pa::kValuMaxD);
+  if (block_ids && num_ids < 0) return fail(PA_ERR_INVALID_ARG, "num_ids %d < 0", num_ids);
+  const char* kr = (const char*)k_rows;
+  const char* kc = (const char*)k_cache;
+  const int es = kv_format == PA_KV_FP8_E4M3 ? 1 : (dtype == PA_F32 ? 4 : 2);
+  const uint64_t bytes = (uint64_t)num_blocks * num_kv_heads * block_size * head_dim * es;
+  const char* vr = (const char*)v_rows;
+  const char* vc = (const char*)v_cache;
+  auto overlap = [bytes](const char* x, const char* y) { return x < y + bytes && y < x + bytes; };
+  if (overlap(kr, kc) || overlap(vr, vc) || overlap(kr, vc) || overlap(vr, kc))
+    return fail(PA_ERR_INVALID_ARG, "the row-layout and tiled caches must not overlap");
+  const int n = block_ids ? num_ids : num_blocks;
+  if (n == 0) return PA_OK;
+  if (n > 65535 * 1024) return fail(PA_ERR_UNSUPPORTED, "%d blocks in one call", n);
+  pa::PackArgs a = {};
+  a.k_rows = (const uint8_t*)k_rows;
+  a.v_rows = (const uint8_t*)v_rows;
+  a.k_cache = (uint8_t*)k_cache;
+  a.v_cache = (uint8_t*)v_cache;
+  a.block_ids = block_ids;
+  a.num_blocks = num_blocks;
+  a.num_kv_heads = num_kv_heads;
+  a.log2_bs = ilog2_exact(block_size);
+  a.head_dim = head_dim;
+  a.es = es;
+  hipLaunchKernelGGL(pa::pack_kv, dim3(num_kv_heads, n), dim3(256), 0, (hipStream_t)hip_stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "pack_kv launch");
+  return PA_OK;
+}
 
 pa_status pa_debug_spans(const int32_t* block_tables, const int32_t* seq_lens,
                          const int32_t* query_lens, int32_t window, int32_t num_kv_heads,

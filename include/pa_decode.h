@@ -217,6 +217,10 @@ pa_status pa_decode_workspace_size_ex(const pa_dims* dims, int32_t window, int32
  *   window     0 (unlimited causal) or the window length in positions
  *   workspace  device scratch of at least pa_decode_workspace_size() bytes,
  *              256-byte aligned; may be NULL when that size is 0
+ * pa_decode keeps the argument list of the interface it follows, which has
+ * no place for FP8 scales: a call on an FP8 cache or with FP8 queries (whose
+ * scales must be given, never defaulted) returns PA_ERR_INVALID_ARG and must
+ * go through pa_decode_ex with pa_options.k_scale / v_scale / q_scale.
  *   hip_stream hipStream_t or NULL
  */
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -255,6 +259,26 @@ pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const
 
 /* Size in bytes of pa_decode_noalloc's static scratch. */
 size_t pa_noalloc_scratch_bytes(void);
+
+/*
+ * Repacks a paged KV cache held one row per slot, k_rows and v_rows
+ * [num_blocks, H_kv, block_size, D] (the plain layout of gllm #116 "What
+ * changes — Interface"), into the tiled k_cache / v_cache layouts above, on
+ * the given stream: a byte permutation, so the values are bit-identical.
+ *   block_ids  device int32 array of the num_ids physical blocks to repack
+ *              (ids outside [0, num_blocks) are skipped), or NULL for all
+ *              num_blocks blocks; blocks not repacked are left untouched
+ *   dtype, kv_format   element type as in pa_dims (fp32, bf16 or E4M3 codes)
+ * Head dims off the column grid (not a multiple of 8, or of 16 for FP8) keep
+ * one row per slot in K, so K is copied as it is.  All four caches are
+ * device memory, 16-byte aligned, and the row-layout caches must not
+ * overlap the tiled ones.  The library allocates nothing; errors as
+ * pa_decode.
+ */
+pa_status pa_pack_kv_cache(const void* k_rows, const void* v_rows, void* k_cache, void* v_cache,
+                           const int32_t* block_ids, int32_t num_ids, int32_t num_blocks,
+                           int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                           int32_t dtype, int32_t kv_format, void* hip_stream);
 
 /*
  * Index dump for bit-exact checks: runs the device index helpers the

@@ -370,3 +370,24 @@ def test_check_inputs_rejects_null_pointers(lib):
     for args in ((None, z, z, z), (z, None, z, z), (z, z, None, z), (z, z, z, None)):
         st = lib.pa_check_inputs(args[0], args[1], args[2], 0, 1, 16, ctypes.byref(d), args[3], None)
         assert st == pa.ERR_INVALID_ARG
+
+
+def test_pack_rejects_bad_arguments_before_any_launch(lib):
+    """Host-side validation of pa_pack_kv_cache (no device touched)."""
+    P = ctypes.c_void_p
+    MB = 1 << 20
+
+    def call(k=P(4096), v=P(4096 + 64 * MB), kc=P(4096 + 128 * MB), vc=P(4096 + 192 * MB),
+             ids=None, n=0, nb=4, h=2, bs=16, D=128, dtype=pa.BF16, fmt=pa.KV_NATIVE):
+        return lib.pa_pack_kv_cache(k, v, kc, vc, ids, n, nb, h, bs, D, dtype, fmt, None)
+
+    assert call(k=None) == pa.ERR_INVALID_ARG
+    assert call(k=P(4100)) == pa.ERR_INVALID_ARG                  # misaligned
+    assert call(kc=P(4096 + 1024)) == pa.ERR_INVALID_ARG          # overlaps k_rows
+    assert call(dtype=5) == pa.ERR_INVALID_ARG
+    assert call(fmt=3) == pa.ERR_INVALID_ARG
+    assert call(bs=8) == pa.ERR_UNSUPPORTED
+    assert call(D=300) == pa.ERR_UNSUPPORTED
+    assert call(nb=0) == pa.ERR_INVALID_ARG
+    assert call(ids=P(4096 + 256 * MB), n=-1) == pa.ERR_INVALID_ARG
+    assert call(ids=P(4096 + 256 * MB), n=0) == pa.OK               # nothing listed: no launch
