@@ -52,8 +52,8 @@ def kernel_source_hash() -> str:
     from decode_attention_pa_amd import build as b
     d = os.path.join(ROOT, "decode_attention_pa_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("pa_common.h", "pa_mfma.h", "pa_valu.h", "pa_launch.h", "pa_decode.hip",
-              "pa_mfma_d64.hip", "pa_mfma_d128.hip", "pa_mfma_d256.hip"):
+    for f in ("pa_common.h", "pa_mfma.h", "pa_valu.h", "pa_wave.h", "pa_launch.h", "pa_decode.hip",
+              "pa_mfma_d64.hip", "pa_mfma_d128.hip", "pa_mfma_d256.hip", "pa_wave_kernels.hip"):
         src = open(os.path.join(d, f), encoding="utf-8").read()
         if f == "pa_decode.hip":
             src = src.split('extern "C" {')[0]
@@ -275,7 +275,8 @@ def pct(xs, p):
 
 def make_call(pa, case, window, a, events=(None, None)):
     w = case.w
-    path = {"auto": 0, "valu": pa.PATH_VALU, "mfma": pa.PATH_MFMA}[a.path]
+    path = {"auto": 0, "valu": pa.PATH_VALU, "mfma": pa.PATH_MFMA,
+            "valu-lds": pa.PATH_VALU_LDS}[a.path]
     return pa.Prepared(case.new_out(), case.q, case.k_cache, case.v_cache, case.block_tables,
                        case.seq_lens, case.query_lens, case.scale, window, w.num_kv_heads,
                        w.block_size, max_seq_len=w.max_seq_len, max_query_len=w.query_len,
@@ -376,7 +377,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--window", type=int, default=None)
-    ap.add_argument("--path", default="auto", choices=["auto", "mfma", "valu"])
+    ap.add_argument("--path", default="auto", choices=["auto", "mfma", "valu", "valu-lds"])
     ap.add_argument("--part-size", type=int, default=0)
     ap.add_argument("--waves", type=int, default=0)
     ap.add_argument("--schedule", default="auto", choices=["auto", "grid", "persistent"])

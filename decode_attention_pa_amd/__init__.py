@@ -22,14 +22,15 @@ import os
 
 __all__ = [
     "PaError", "Dims", "Plan", "Options", "load", "library_path", "plan", "workspace_size",
-    "decode", "debug_spans", "check_inputs", "PATH_AUTO", "PATH_VALU", "PATH_MFMA", "F32", "BF16",
+    "decode", "debug_spans", "check_inputs", "PATH_AUTO", "PATH_VALU", "PATH_MFMA",
+    "PATH_VALU_LDS", "F32", "BF16",
     "EXPORTED_SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpa_decode.so")
 
-PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
+PATH_AUTO, PATH_VALU, PATH_MFMA, PATH_VALU_LDS = 0, 1, 2, 3
 F32, BF16 = 0, 1
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 
@@ -56,7 +57,7 @@ class Dims(ctypes.Structure):
 
 class Plan(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("rows", ctypes.c_int32),
-                ("span_max", ctypes.c_int32), ("part_size", ctypes.c_int32),
+                ("block_rows", ctypes.c_int32), ("span_max", ctypes.c_int32), ("part_size", ctypes.c_int32),
                 ("num_parts", ctypes.c_int32), ("waves", ctypes.c_int32),
                 ("one_shot", ctypes.c_int32), ("persistent", ctypes.c_int32),
                 ("row_tiles", ctypes.c_int32), ("row_blocks", ctypes.c_int32),

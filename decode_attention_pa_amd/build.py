@@ -19,7 +19,8 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libpa_decode.so")
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = [os.path.join(CSRC, f) for f in
-           ("pa_decode.hip", "pa_mfma_d64.hip", "pa_mfma_d128.hip", "pa_mfma_d256.hip")]
+           ("pa_decode.hip", "pa_mfma_d64.hip", "pa_mfma_d128.hip", "pa_mfma_d256.hip",
+            "pa_wave_kernels.hip")]
 HEADERS = [os.path.join(ROOT, "include", "pa_decode.h")] + [
     os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC)) if f.endswith(".h")]
 

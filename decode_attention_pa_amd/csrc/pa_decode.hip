@@ -164,16 +164,19 @@ pa_status make_plan(const pa_dims* d, int32_t window, int32_t hkv, int32_t bs, i
   r.span_max = window ? (int32_t)std::min<int64_t>(d->max_seq_len, (int64_t)window + d->max_query_len - 1)
                       : d->max_seq_len;
   const int path_req = o ? o->path : PA_PATH_AUTO;
-  if (path_req < PA_PATH_AUTO || path_req > PA_PATH_MFMA)
+  if (path_req < PA_PATH_AUTO || path_req > PA_PATH_VALU_LDS)
     return fail(PA_ERR_INVALID_ARG, "path %d unknown", path_req);
   if (path_req == PA_PATH_AUTO) {
-    // fp32 inputs never take reduced-precision products.  For bf16 the matrix
-    // cores are faster than the vector kernel at every row count measured on
-    // MI355X (R = 4 included); other head dims take the vector kernel.
+    // fp32 inputs never take reduced-precision products: the vector ALUs.
+    // For bf16 the matrix cores, which measured faster than the vector
+    // kernels on MI355X at every row count (R = 4 included).
     r.path = (d->dtype == PA_F32 || !mfma_head_dim(d->head_dim)) ? PA_PATH_VALU : PA_PATH_MFMA;
   } else {
     r.path = path_req;
   }
+  // the register-resident vector kernel is instantiated at head dims 64, 128
+  // and 256; other head dims stage K and V through shared memory
+  if (r.path == PA_PATH_VALU && !mfma_head_dim(d->head_dim)) r.path = PA_PATH_VALU_LDS;
   if (r.path == PA_PATH_MFMA && d->dtype != PA_BF16)
     return fail(PA_ERR_UNSUPPORTED, "the matrix-core path needs bf16 inputs");
   if (r.path == PA_PATH_MFMA && !mfma_head_dim(d->head_dim))
@@ -193,18 +196,29 @@ pa_status make_plan(const pa_dims* d, int32_t window, int32_t hkv, int32_t bs, i
     if (w_req) {
       if (w_req != 1 && w_req != 2 && w_req != 4)
         return fail(PA_ERR_INVALID_ARG, "waves %d must be 1, 2 or 4", w_req);
-      if (w_req * r.row_tiles > 4)
-        return fail(PA_ERR_UNSUPPORTED, "waves %d x row tiles %d exceeds 4", w_req, r.row_tiles);
+      // two row tiles also run with 4 waves (each K/V load feeds both tiles)
+      if (w_req * r.row_tiles > (r.row_tiles == 2 ? 8 : 4))
+        return fail(PA_ERR_UNSUPPORTED, "waves %d x row tiles %d not instantiated", w_req,
+                    r.row_tiles);
       r.waves = w_req;
     } else {
       r.waves = r.row_tiles == 1 ? 4 : (r.row_tiles == 2 ? 2 : 1);
     }
-    r.row_blocks = (r.rows + 16 * r.row_tiles - 1) / (16 * r.row_tiles);
+    r.block_rows = 16 * r.row_tiles;
+  } else if (r.path == PA_PATH_VALU) {
+    r.waves = 4;  // 256-thread workgroup
+    r.row_tiles = 0;
+    // rows per workgroup: 4 or 8 (the scores of a step take one register
+    // per row, and at least 4 independent accumulators keep the broadcast
+    // multiply-adds free of read-after-write waits; fewer real rows leave
+    // zero rows, which cost arithmetic but no memory traffic)
+    r.block_rows = r.rows <= 4 ? 4 : 8;
   } else {
     r.waves = 4;  // 256-thread workgroup
     r.row_tiles = pa::kValuRows / 16;
-    r.row_blocks = (r.rows + pa::kValuRows - 1) / pa::kValuRows;
+    r.block_rows = pa::kValuRows;
   }
+  r.row_blocks = (r.rows + r.block_rows - 1) / r.block_rows;
   const int64_t span_cover = (int64_t)r.span_max + pa::kChunk - 1;  // span plus alignment slack
   const int64_t units = (int64_t)d->batch * hkv;
   const int sched_req = o ? o->schedule : 0;
@@ -302,6 +316,7 @@ pa_status make_plan(const pa_dims* d, int32_t window, int32_t hkv, int32_t bs, i
         units * r.row_blocks * r.waves < 16 * (int64_t)num_cus) {
       r.row_tiles = 1;
       r.waves = 4;
+      r.block_rows = 16;
       r.row_blocks = (r.rows + 15) / 16;
     }
     // Split plans at head dim 256 (~250 VGPRs, one or two waves per SIMD):
@@ -394,7 +409,7 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
                  "P=%d NP=%d waves=%d row_tiles=%d row_blocks=%d one_shot=%d persistent=%d "
                  "ps_grid=%d streaming=%d ws=%llu cus=%d\n",
                  d->batch, d->num_q_heads, hkv, d->head_dim, bs, window, (int)kv8, (int)q8, p.rows,
-                 p.span_max, p.path == PA_PATH_MFMA ? "mfma" : "valu", p.part_size, p.num_parts,
+                 p.span_max, p.path == PA_PATH_MFMA ? "mfma" : (p.path == PA_PATH_VALU ? "valu" : "valu-lds"), p.part_size, p.num_parts,
                  p.waves, p.row_tiles, p.row_blocks, p.one_shot, p.persistent, p.ps_grid, p.streaming,
                  (unsigned long long)p.workspace_bytes, cus);
 
@@ -449,12 +464,16 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
       case 128: ok = pa_host::launch_mfma_128(nrt, p.waves, grid, p.persistent, p.streaming, kv8, q8, cus, L, a); break;
       default: ok = pa_host::launch_mfma_256(nrt, p.waves, grid, p.persistent, p.streaming, kv8, q8, cus, L, a); break;
     }
+  } else if (p.path == PA_PATH_VALU) {
+    ok = pa_host::launch_wave(d->dtype == PA_F32, d->head_dim, p.block_rows, grid, L, a);
   } else if (d->dtype == PA_F32) {
     launch_part(pa::part_valu<float>, grid, dim3(256), L, a);
   } else {
     launch_part(pa::part_valu<uint16_t>, grid, dim3(256), L, a);
   }
-  if (!ok) return fail(PA_ERR_UNSUPPORTED, "no kernel for %d row tiles x %d waves", nrt, p.waves);
+  if (!ok)
+    return fail(PA_ERR_UNSUPPORTED, "no kernel for %d row tiles / %d rows x %d waves", nrt,
+                p.block_rows, p.waves);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "partition kernel launch");
   if (!p.one_shot) {

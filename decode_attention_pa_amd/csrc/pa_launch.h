@@ -65,6 +65,7 @@ bool launch_mfma_shape(int nrt, int nw, dim3 grid, bool persistent, int cus, con
     case 1 * 8 + 4: launch_mfma_inst<D, 1, 4, STREAM, KV8, Q8>(grid, persistent, cus, L, a); return true;
     case 2 * 8 + 1: launch_mfma_inst<D, 2, 1, STREAM, KV8, Q8>(grid, persistent, cus, L, a); return true;
     case 2 * 8 + 2: launch_mfma_inst<D, 2, 2, STREAM, KV8, Q8>(grid, persistent, cus, L, a); return true;
+    case 2 * 8 + 4: launch_mfma_inst<D, 2, 4, STREAM, KV8, Q8>(grid, persistent, cus, L, a); return true;
     case 3 * 8 + 1: launch_mfma_inst<D, 3, 1, STREAM, KV8, Q8>(grid, persistent, cus, L, a); return true;
     case 4 * 8 + 1: launch_mfma_inst<D, 4, 1, STREAM, KV8, Q8>(grid, persistent, cus, L, a); return true;
     default: return false;
@@ -93,5 +94,9 @@ bool launch_mfma_128(int nrt, int nw, dim3 grid, bool persistent, bool streaming
                      int cus, const Launch& L, const pa::PartArgs& a);
 bool launch_mfma_256(int nrt, int nw, dim3 grid, bool persistent, bool streaming, bool kv8, bool q8,
                      int cus, const Launch& L, const pa::PartArgs& a);
+
+// Register-resident vector kernels (pa_wave_kernels.hip): fp32 or bf16
+// caches, head dims 64, 128 and 256, 4 or 8 rows per workgroup.
+bool launch_wave(bool f32, int D, int block_rows, dim3 grid, const Launch& L, const pa::PartArgs& a);
 
 }  // namespace pa_host

@@ -132,14 +132,20 @@ typedef struct pa_dims {
 /* Kernel families for the partition step. */
 typedef enum pa_path {
   PA_PATH_AUTO = 0,
-  PA_PATH_VALU = 1,           /* vector-ALU dot products; any dtype */
-  PA_PATH_MFMA = 2            /* bf16 matrix cores (16-row tiles); bf16 only */
+  PA_PATH_VALU = 1,           /* vector ALUs, register-resident: lane = position for QK^T,
+                                 lane = output dims for PV, up to 8 rows per workgroup;
+                                 fp32 or bf16 caches at head dims 64, 128 and 256 (other
+                                 head dims fall back to PA_PATH_VALU_LDS) */
+  PA_PATH_MFMA = 2,           /* bf16 matrix cores (16-row tiles); bf16 only */
+  PA_PATH_VALU_LDS = 3        /* vector ALUs with K and V staged through shared memory,
+                                 16 rows per workgroup; any head dim up to 256 */
 } pa_path;
 
 /* Launch plan: a pure function of the arguments below and the CU count. */
 typedef struct pa_plan {
-  int32_t path;               /* PA_PATH_VALU or PA_PATH_MFMA */
+  int32_t path;               /* PA_PATH_VALU, PA_PATH_MFMA or PA_PATH_VALU_LDS */
   int32_t rows;               /* R = G * max_query_len rows per KV head */
+  int32_t block_rows;         /* packed rows per workgroup (row_blocks = ceil(R / block_rows)) */
   int32_t span_max;           /* longest windowed span over the batch bound */
   int32_t part_size;          /* positions per partition, a multiple of 32 */
   int32_t num_parts;          /* partition-grid extent per (sequence, KV head) */

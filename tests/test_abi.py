@@ -84,6 +84,7 @@ def test_plan_covers_longest_span(lib, name):
             assert p["workspace_bytes"] == 2 * al(4 * states) + al(4 * states * w.head_dim) + runs
             assert p["ps_grid"] > 0 if p["persistent"] else p["ps_grid"] == 0
         expect_path = pa.PATH_VALU if w.dtype == "f32" else pa.PATH_MFMA
+        assert p["row_blocks"] == -(-p["rows"] // p["block_rows"])
         assert p["path"] == expect_path
 
 
@@ -140,10 +141,22 @@ def test_general_rows_and_head_dims(lib):
     assert (p["path"], p["row_tiles"], p["row_blocks"], p["waves"]) == (pa.PATH_MFMA, 1, 1, 2)
     p = pa.plan(dims_of(w, max_query_len=5, head_dim=256), 0, 8, 16)    # 20 rows, D = 256
     assert (p["row_tiles"], p["row_blocks"]) == (1, 2)
-    p = pa.plan(dims_of(w, head_dim=66), 0, 8, 16)                   # odd head dim
-    assert (p["path"], p["row_tiles"], p["row_blocks"]) == (pa.PATH_VALU, 1, 1)
+    p = pa.plan(dims_of(w, head_dim=66), 0, 8, 16)                   # odd head dim: staged
+    assert (p["path"], p["block_rows"], p["row_blocks"]) == (pa.PATH_VALU_LDS, 16, 1)
     p = pa.plan(dims_of(w, head_dim=66, max_query_len=9), 0, 8, 16)  # 36 rows
     assert p["row_blocks"] == 3
+    # the register-resident vector kernel: 4 or 8 rows per workgroup
+    f = dict(dtype=pa.F32)
+    p = pa.plan(dims_of(w, **f), 0, 8, 16)                             # fp32, 4 rows
+    assert (p["path"], p["block_rows"], p["row_blocks"]) == (pa.PATH_VALU, 4, 1)
+    p = pa.plan(dims_of(w, max_query_len=9, **f), 0, 8, 16)            # fp32, 36 rows
+    assert (p["path"], p["block_rows"], p["row_blocks"]) == (pa.PATH_VALU, 8, 5)
+    p = pa.plan(dims_of(w, head_dim=64), 0, 8, 16, path=pa.PATH_VALU)  # bf16 on request
+    assert (p["path"], p["block_rows"]) == (pa.PATH_VALU, 4)
+    p = pa.plan(dims_of(w, head_dim=200, **f), 0, 8, 16, path=pa.PATH_VALU)  # no such kernel
+    assert (p["path"], p["block_rows"]) == (pa.PATH_VALU_LDS, 16)
+    p = pa.plan(dims_of(w, **f), 0, 8, 16, path=pa.PATH_VALU_LDS)      # staged on request
+    assert (p["path"], p["block_rows"]) == (pa.PATH_VALU_LDS, 16)
     with pytest.raises(pa.PaError) as e:                             # no matrix-core kernel
         pa.plan(dims_of(w, head_dim=66), 0, 8, 16, path=pa.PATH_MFMA)
     assert e.value.status == pa.ERR_UNSUPPORTED

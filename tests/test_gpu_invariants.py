@@ -32,9 +32,9 @@ from tests._gpu_util import BF16_TOL, compare, oracle_out, run_gpu, say
 
 pytestmark = pytest.mark.gpu
 
-PATHS = [pa.PATH_MFMA, pa.PATH_VALU]
+PATHS = [pa.PATH_MFMA, pa.PATH_VALU, pa.PATH_VALU_LDS]
 KERNELS = [(pa.PATH_MFMA, pa.SCHED_GRID), (pa.PATH_MFMA, pa.SCHED_PERSISTENT),
-           (pa.PATH_VALU, pa.SCHED_GRID)]
+           (pa.PATH_VALU, pa.SCHED_GRID), (pa.PATH_VALU_LDS, pa.SCHED_GRID)]
 
 
 @pytest.fixture(autouse=True)

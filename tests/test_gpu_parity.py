@@ -57,7 +57,7 @@ def test_tiny_f32(window):
 
 
 KERNELS = [(pa.PATH_MFMA, pa.SCHED_GRID), (pa.PATH_MFMA, pa.SCHED_PERSISTENT),
-           (pa.PATH_VALU, pa.SCHED_GRID)]
+           (pa.PATH_VALU, pa.SCHED_GRID), (pa.PATH_VALU_LDS, pa.SCHED_GRID)]
 
 
 @pytest.mark.parametrize("path,sched", KERNELS)
@@ -349,3 +349,33 @@ def test_graph_replays_match_eager():
             assert torch.equal(out_g, eager), (o, rep)
             assert torch.equal(run_gpu(c, workspace=ws, **o), eager), (o, rep)
         say(f"[graph] {o}: 3 replays identical to eager")
+
+
+@pytest.mark.parametrize("sched", [pa.SCHED_GRID, pa.SCHED_PERSISTENT])
+@pytest.mark.parametrize("D", [64, 128])
+def test_two_tiles_four_waves(D, sched):
+    """32 packed rows per KV head in one workgroup of 4 waves (each K/V load
+    feeds both 16-row tiles), windowed and full, split and one-shot."""
+    w = small(8, head_dim=D, num_q_heads=16, num_kv_heads=2, query_len=4, batch=3,
+              seq_lens=(700, 129, 40), block_size=64, max_seq_len=700, max_blocks_per_seq=12)
+    for win in (0, 5, 128):
+        c = workloads.make_case(w, device="cuda", window=win)
+        exp, rows = oracle_out(c)
+        for P in (0, 64, 1024):
+            compare(run_gpu(c, path=pa.PATH_MFMA, waves=4, part_size=P, schedule=sched), exp, rows,
+                    BF16_TOL, f"2 tiles x 4 waves D={D} sched={sched} w={win} P={P}")
+
+
+@pytest.mark.parametrize("name,nsample", [("gqa_f32", 8), ("long_splitk_bf16", None)])
+def test_vector_kernel_full_size(name, nsample):
+    """The register-resident vector kernel at full size: the fp32 GQA batch
+    (its automatic path) at the fp32 bars, and the single 131072-position
+    bf16 sequence forced onto it."""
+    w = workloads.WORKLOADS[name]
+    c = workloads.make_case(w, device="cuda", window=0)
+    out = run_gpu(c, path=pa.PATH_VALU)
+    seqs = sample_sequences(c.seq_lens_host, nsample, w.seed)
+    exp, rows = oracle_out(c, seqs)
+    compare(out, exp, rows, F32_TOL if w.dtype == "f32" else BF16_TOL,
+            f"vector kernel {name} seqs={len(seqs)}")
+    assert torch.isfinite(out.float()).all()

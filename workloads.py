@@ -101,6 +101,13 @@ WORKLOADS = {
         max_seq_len=131072, seq_lens=(131072,), pool=10240,
         description="single-KV-group long-context split-K decode bf16: B=1, "
                     "8/1 heads, D=128, bs=16, context 131072, q_len 1, window 0"),
+    "gqa_f32": Workload(
+        name="gqa_f32", dtype="f32", batch=32, num_q_heads=32, num_kv_heads=8,
+        head_dim=128, block_size=16, query_len=1, windows=(0,),
+        scale=1.0 / math.sqrt(128.0), seed=2, max_blocks_per_seq=512,
+        max_seq_len=8192, len_range=(512, 8192),
+        description="GQA decode fp32 (the GQA batch in float32): B=32, 32/8 heads, D=128, "
+                    "bs=16, context U[512, 8192], q_len 1, window 0"),
     "gqa_fp8kv": Workload(
         name="gqa_fp8kv", dtype="bf16", kv_dtype="fp8", batch=32, num_q_heads=32,
         num_kv_heads=8, head_dim=128, block_size=16, query_len=1, windows=(0,),
