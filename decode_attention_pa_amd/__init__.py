@@ -28,7 +28,9 @@ __all__ = [
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libpa_decode.so")
+# the in-tree build, or another build of the same library named by
+# PA_DECODE_LIBRARY (an absolute path)
+_LIB_PATH = os.environ.get("PA_DECODE_LIBRARY") or os.path.join(_HERE, "libpa_decode.so")
 
 PATH_AUTO, PATH_VALU, PATH_MFMA, PATH_VALU_LDS = 0, 1, 2, 3
 F32, BF16 = 0, 1
