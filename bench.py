@@ -16,8 +16,9 @@ timed calls), achieved HBM GB/s of the partition kernel on algorithmic bytes
 roofline fraction of MI355X's 8 TB/s, the float64 CPU oracle timed on the
 host's cores over a bounded sample of the same workload, and (``side``) the
 other workloads' per-call figures measured in the same run: the GQA batch,
-the single 131072-position sequence and the sliding-window MTP batch cold
-(flushed), and the large-block batch at window 4096.
+the single 131072-position sequence, the sliding-window MTP batch and the
+GQA batch in fp32 (vector-ALU kernel) cold (flushed), and the large-block
+batch at window 4096.
 
 Algorithmic bytes per call (what the method must move): for every
 (sequence, KV head) the K and V bytes of the union of its rows' visible
@@ -343,7 +344,7 @@ def summary(per, kern, nb) -> dict:
 # (a 1 GiB read before each call, outside its events), as a decode step over
 # many layers meets them.
 SIDE = (("gqa_bf16", 0, True), ("long_splitk_bf16", 0, True), ("swa_mtp_bf16", 128, True),
-        ("large_block_mtp_bf16", 4096, False))
+        ("large_block_mtp_bf16", 4096, False), ("gqa_f32", 0, True))
 
 
 def side_lines(pa, workloads, main_case, a, flush_buf, reps) -> dict:

@@ -96,6 +96,19 @@ __device__ inline int wave_row_offset(const int32_t* __restrict__ query_lens, in
   return s;
 }
 
+// Batches above this size get their row offsets from a prefix array that a
+// one-workgroup scan writes into the workspace before the partition kernel
+// (below it every workgroup sums query_lens[0 .. b) itself, which costs
+// O(B) per workgroup).
+constexpr int kScanBatch = 1024;
+
+// First q/out row of sequence b: from the scanned prefix array when there is
+// one, else summed by the calling wave.
+__device__ inline int row_offset(const int32_t* __restrict__ qoffs,
+                                 const int32_t* __restrict__ query_lens, int b) {
+  return qoffs ? qoffs[b] : wave_row_offset(query_lens, b);
+}
+
 __device__ inline float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
@@ -133,6 +146,7 @@ struct PartArgs {
   const float* k_scale;        // FP8 KV: device scalars, K = code * k_scale, V = code * v_scale
   const float* v_scale;        // (null for native caches)
   const float* q_scale;        // FP8 Q: device scalar, Q = code * q_scale (else null)
+  const int32_t* qoffs;        // [B] exclusive prefix of query_lens (batches > kScanBatch), or null
 };
 
 // Work-item of a partition workgroup.  The grid is 1-D and ordered with the
@@ -186,6 +200,7 @@ struct ReduceArgs {
   int num_parts;
   int part_size;
   int head_dim;
+  const int32_t* qoffs;  // [B] exclusive prefix of query_lens, or null
 };
 
 }  // namespace pa

@@ -135,20 +135,24 @@ pa_status check_shape(const pa_dims* d, int32_t window, int32_t num_kv_heads, in
 // normalised output, 256-byte aligned regions; the persistent schedule adds
 // a (run count, first slot) pair per unit.  Slots: one per (unit, partition)
 // on the grid schedule, persistent grid + units on the persistent one.
+// Workspace: partial states of split plans (none for one-shot plans), the
+// persistent schedule's per-unit run records, and for batches above
+// kScanBatch the scanned row offsets.
 struct WsLayout {
   uint64_t states;  // state rows (slots x R)
-  uint64_t off_l, off_o, off_runs, total;
+  uint64_t off_l, off_o, off_runs, off_qoffs, total;
 };
 
 WsLayout workspace_layout(const pa_plan& r, const pa_dims& d, int hkv) {
   WsLayout w;
   const uint64_t units = (uint64_t)d.batch * hkv;
-  const uint64_t slots = r.persistent ? (uint64_t)r.ps_grid + units : units * r.num_parts;
+  const uint64_t slots = r.one_shot ? 0 : (r.persistent ? (uint64_t)r.ps_grid + units : units * r.num_parts);
   w.states = slots * r.rows;
   w.off_l = align256(w.states * 4);
   w.off_o = w.off_l + align256(w.states * 4);
   w.off_runs = w.off_o + align256(w.states * d.head_dim * 4);
-  w.total = w.off_runs + (r.persistent ? align256(units * 8) : 0);
+  w.off_qoffs = w.off_runs + (r.persistent && !r.one_shot ? align256(units * 8) : 0);
+  w.total = w.off_qoffs + (d.batch > pa::kScanBatch ? align256((uint64_t)d.batch * 4) : 0);
   return w;
 }
 
@@ -332,11 +336,7 @@ pa_status make_plan(const pa_dims* d, int32_t window, int32_t hkv, int32_t bs, i
     const bool kv8 = d->kv_format == PA_KV_FP8_E4M3;
     r.ps_grid = pa::ps_wgs_per_cu(d->head_dim, r.row_tiles, r.waves, kv8) * num_cus;
   }
-  if (r.one_shot) {
-    r.workspace_bytes = 0;
-  } else {
-    r.workspace_bytes = workspace_layout(r, *d, hkv).total;
-  }
+  r.workspace_bytes = workspace_layout(r, *d, hkv).total;
   *p = r;
   return PA_OK;
 }
@@ -427,6 +427,7 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
   a.ws_l = p.one_shot ? nullptr : (float*)(ws + wl.off_l);
   a.ws_o = p.one_shot ? nullptr : (float*)(ws + wl.off_o);
   a.ws_runs = (p.one_shot || !p.persistent) ? nullptr : (int*)(ws + wl.off_runs);
+  a.qoffs = d->batch > pa::kScanBatch ? (const int32_t*)(ws + wl.off_qoffs) : nullptr;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.window = window;
   a.num_q_heads = d->num_q_heads;
@@ -448,6 +449,12 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
   hipError_t e;
   const Launch L = {s, o ? (hipEvent_t)o->event_begin : nullptr,
                    o ? (hipEvent_t)o->event_end : nullptr};
+  if (a.qoffs) {
+    hipLaunchKernelGGL(pa::scan_row_offsets, dim3(1), dim3(1024), 0, s, query_lens, d->batch,
+                       (int32_t*)a.qoffs);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "row offset scan launch");
+  }
   const uint64_t units = (uint64_t)p.num_parts * hkv * d->batch;  // (partition, seq, head)
   const uint64_t nwg = p.row_blocks > 1
                            ? (units + pa::kXcds - 1) / pa::kXcds * pa::kXcds * p.row_blocks
@@ -493,6 +500,7 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
     r.num_parts = p.num_parts;
     r.part_size = p.part_size;
     r.head_dim = d->head_dim;
+    r.qoffs = a.qoffs;
     // persistent: a unit has one state per workgroup share it crosses;
     // balanced units cross about (grid / units) + 2 shares (a lone long unit
     // crosses them all)

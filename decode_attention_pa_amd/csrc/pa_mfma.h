@@ -556,7 +556,7 @@ __global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
   if (it.j >= sv.nparts) return;  // empty partition: contributes nothing
   const int r0 = it.rb * 16 * NRT;                // first packed row of this block
   if (r0 >= a.group * q) return;                 // no row of this sequence is in it
-  const int qoff = wave_row_offset(a.query_lens, it.b);
+  const int qoff = row_offset(a.qoffs, a.query_lens, it.b);
   const size_t state = ((size_t)it.b * a.num_kv_heads + it.h) * a.num_parts + it.j;
   mfma_run<D, NRT, NW, STREAM, KV8, Q8, false>(a, it.b, it.h, L, q, qoff, sv, it.j, it.j, state,
                                                sv.nparts == 1, r0);

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void lse_reduce(ReduceArgs a) {
   // persistent schedule: the unit's run count and first state slot
   const int2 rs = a.ws_runs ? *(const int2*)(a.ws_runs + 2 * ((size_t)b * a.num_kv_heads + h))
                             : make_int2(0, 0);
-  const int qoff = wave_row_offset(a.query_lens, b);  // all lanes still active
+  const int qoff = row_offset(a.qoffs, a.query_lens, b);  // all lanes still active
   const int G = a.group;
   const SeqView sv = seq_view(L, q, a.window, a.part_size);
   // states to merge: one per partition, or the unit's run count
@@ -136,6 +136,32 @@ __global__ __launch_bounds__(256) void lse_reduce(ReduceArgs a) {
   T* op = (T*)a.out + ((size_t)(qoff + i) * a.num_q_heads + (size_t)h * G + g) * D + d4 * VEC;
 #pragma unroll
   for (int e = 0; e < VEC; ++e) store_elem<T>(op + e, acc[e] * inv);
+}
+
+// Exclusive prefix sum of query_lens[0 .. B) into qoffs (one workgroup of
+// 1024 threads: per-thread runs, a wave scan, then the waves in order).
+__global__ __launch_bounds__(1024) void scan_row_offsets(const int32_t* __restrict__ query_lens,
+                                                         int B, int32_t* __restrict__ qoffs) {
+  __shared__ int s_wave[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = (B + 1023) / 1024;
+  const int k0 = min(B, tid * per), k1 = min(B, k0 + per);
+  int cnt = 0;
+  for (int k = k0; k < k1; ++k) cnt += query_lens[k];
+  int inc = cnt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(inc, off);
+    if (lane >= off) inc += t;
+  }
+  if (lane == 63) s_wave[wave] = inc;
+  __syncthreads();
+  int run = inc - cnt;
+  for (int w = 0; w < wave; ++w) run += s_wave[w];
+  for (int k = k0; k < k1; ++k) {
+    qoffs[k] = run;
+    run += query_lens[k];
+  }
 }
 
 // Partition lanes per output unit for a given number of states per unit.

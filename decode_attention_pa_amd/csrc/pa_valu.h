@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void part_valu(PartArgs a) {
   partition_range(sv, j, a.part_size, &ps, &pe);
   const int cb0 = sv.base + j * a.part_size;
   const int nsub = (pe - cb0 + SUB - 1) / SUB;
-  const int qoff = wave_row_offset(a.query_lens, b);
+  const int qoff = row_offset(a.qoffs, a.query_lens, b);
   const int log2_bs = a.log2_bs;
   const int bs_mask = (1 << log2_bs) - 1;
   const bool k_rows = (D & 7) != 0;  // K layout: one row per slot, else 16-slot tiles

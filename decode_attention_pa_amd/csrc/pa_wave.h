@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void part_wave(PartArgs a) {
   partition_range(sv, j, a.part_size, &ps, &pe);
   const int cb0 = sv.base + j * a.part_size;  // multiple of 32
   const int nst = (pe - cb0 + 63) / 64;
-  const int qoff = __builtin_amdgcn_readfirstlane(wave_row_offset(a.query_lens, b));
+  const int qoff = __builtin_amdgcn_readfirstlane(row_offset(a.qoffs, a.query_lens, b));
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int log2_bs = a.log2_bs;

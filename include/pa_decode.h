@@ -161,11 +161,14 @@ typedef struct pa_plan {
                                  path) */
   int32_t ps_grid;            /* persistent schedule: most workgroups its grid may hold
                                  (fewer when fewer fit on the device at once); 0 otherwise */
-  uint64_t workspace_bytes;   /* bytes pa_decode needs in `workspace` (0 if one_shot):
-                                 partial states of B*H_kv*num_parts slots on the grid
-                                 schedule, of ps_grid + B*H_kv slots on the persistent one
+  uint64_t workspace_bytes;   /* bytes pa_decode needs in `workspace`: partial states
+                                 of split plans, B*H_kv*num_parts slots on the grid
+                                 schedule, ps_grid + B*H_kv slots on the persistent one
                                  (R rows of D + 2 floats each), plus 8 bytes per
-                                 (sequence, KV head) on the persistent schedule */
+                                 (sequence, KV head) on the persistent schedule, plus 4
+                                 bytes per sequence for batches above 1024 (row offsets
+                                 scanned once per call); 0 for one-shot plans of up to
+                                 1024 sequences */
 } pa_plan;
 
 /* Optional controls for pa_decode_ex / pa_plan_compute (zero = automatic). */

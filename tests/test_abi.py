@@ -74,7 +74,7 @@ def test_plan_covers_longest_span(lib, name):
         assert p["num_parts"] * p["part_size"] >= span + 31
         assert p["one_shot"] == (p["num_parts"] == 1)
         if p["one_shot"]:
-            assert p["workspace_bytes"] == 0
+            assert p["workspace_bytes"] == 0          # batches of at most 1024 sequences
         else:
             units = w.batch * w.num_kv_heads
             slots = p["ps_grid"] + units if p["persistent"] else units * p["num_parts"]
@@ -404,3 +404,19 @@ def test_pack_rejects_bad_arguments_before_any_launch(lib):
     assert call(nb=0) == pa.ERR_INVALID_ARG
     assert call(ids=P(4096 + 256 * MB), n=-1) == pa.ERR_INVALID_ARG
     assert call(ids=P(4096 + 256 * MB), n=0) == pa.OK               # nothing listed: no launch
+
+
+def test_large_batches_scan_row_offsets(lib):
+    """Above 1024 sequences the workspace also holds the scanned row offsets
+    (4 bytes per sequence), one-shot plans included."""
+    w = workloads.WORKLOADS["gqa_bf16"]
+    al = lambda x: (x + 255) // 256 * 256
+    small = pa.plan(dims_of(w, batch=1024, max_seq_len=64, max_blocks_per_seq=4), 0, 8, 16)
+    big = pa.plan(dims_of(w, batch=5000, max_seq_len=64, max_blocks_per_seq=4), 0, 8, 16)
+    assert small["one_shot"] and big["one_shot"]
+    assert small["workspace_bytes"] == 0 and big["workspace_bytes"] == al(4 * 5000)
+    split = pa.plan(dims_of(w, batch=5000, max_seq_len=64, max_blocks_per_seq=4), 0, 8, 16,
+                    part_size=32, schedule=pa.SCHED_GRID)
+    states = 5000 * 8 * split["num_parts"] * split["rows"]
+    assert split["workspace_bytes"] == (2 * al(4 * states) + al(4 * states * 128)
+                                        + al(4 * 5000))

@@ -112,12 +112,14 @@ def test_max_rows_and_edge_lengths():
                             BF16_TOL, f"edges D={D} w={win} path={path} sched={sched} P={P}")
 
 
-@pytest.mark.parametrize("B,sched", [(1024, pa.SCHED_PERSISTENT), (1100, pa.SCHED_AUTO)])
+@pytest.mark.parametrize("B,sched", [(1024, pa.SCHED_PERSISTENT), (1100, pa.SCHED_AUTO),
+                                     (8192, pa.SCHED_AUTO)])
 def test_largest_batches(B, sched):
     """The persistent schedule's largest batch (1024 sequences, its prefix sums
-    in shared memory) and a larger one, which the plan hands to the grid
-    schedule.  Query lengths 0-3 make every row offset a long prefix sum;
-    sampled sequences include the last ones."""
+    in shared memory) and larger ones, which the plan hands to the grid
+    schedule with row offsets scanned once into the workspace.  Query
+    lengths 0-3 make every row offset a long prefix sum; sampled sequences
+    include the last ones."""
     r = np.random.default_rng(B)
     qls = tuple(int(x) for x in r.integers(0, 4, size=B))
     lens = tuple(int(q + x) for q, x in zip(qls, r.integers(1, 400, size=B)))
