@@ -120,7 +120,7 @@ def counter_bytes(rows, name: str) -> dict:
     and averaged over the partition dispatches after the first (cold) one."""
     gib_kib = float(1 << 20)
     rows = sorted(rows)
-    is_part = lambda k: "part_mfma" in k or "part_valu" in k
+    is_part = lambda k: "pa::part_" in k      # part_mfma, part_mfma_ps, part_wave, part_valu
     part = [v for _, k, v in rows if is_part(k)]
     first_part = min((i for i, k, _ in rows if is_part(k)), default=0)
     # the calibration copies are the last CALIB_COPIES large copies before
