@@ -113,16 +113,16 @@ def test_max_rows_and_edge_lengths():
 
 
 @pytest.mark.parametrize("B,sched", [(1024, pa.SCHED_PERSISTENT), (1100, pa.SCHED_AUTO),
-                                     (8192, pa.SCHED_AUTO)])
+                                     (8192, pa.SCHED_AUTO), (65535, pa.SCHED_AUTO)])
 def test_largest_batches(B, sched):
     """The persistent schedule's largest batch (1024 sequences, its prefix sums
     in shared memory) and larger ones, which the plan hands to the grid
     schedule with row offsets scanned once into the workspace.  Query
     lengths 0-3 make every row offset a long prefix sum; sampled sequences
-    include the last ones."""
+    include the last ones; 65535 is the largest batch the library takes."""
     r = np.random.default_rng(B)
     qls = tuple(int(x) for x in r.integers(0, 4, size=B))
-    lens = tuple(int(q + x) for q, x in zip(qls, r.integers(1, 400, size=B)))
+    lens = tuple(int(q + x) for q, x in zip(qls, r.integers(1, 400 if B <= 8192 else 120, size=B)))
     w = small(5, batch=B, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
               query_len=3, seq_lens=lens, query_lens=qls, max_seq_len=max(lens),
               max_blocks_per_seq=-(-max(lens) // 16) + 1)

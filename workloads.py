@@ -44,6 +44,7 @@ from __future__ import annotations
 import math
 from dataclasses import dataclass, field, replace
 
+import numpy as np
 import torch
 
 
@@ -274,12 +275,15 @@ def make_case(w: Workload | str, device="cpu", window: int | None = None,
         used.append(perm[off:off + n])
         off += n
     unused = perm[needed:]
-    tables = torch.full((w.batch, w.max_blocks_per_seq), unused[0], dtype=torch.int32)
-    for b, ids in enumerate(used):
-        if len(ids) > w.max_blocks_per_seq:
-            raise ValueError("max_blocks_per_seq too small for the drawn lengths")
-        if ids:
-            tables[b, :len(ids)] = torch.tensor(ids, dtype=torch.int32)
+    if max(nblk, default=0) > w.max_blocks_per_seq:
+        raise ValueError("max_blocks_per_seq too small for the drawn lengths")
+    # row b holds its blocks' ids in order, then the padding id
+    counts = np.asarray(nblk, dtype=np.int64)
+    rows = np.repeat(np.arange(w.batch), counts)
+    cols = np.arange(needed) - np.repeat(np.cumsum(counts) - counts, counts)
+    tab = np.full((w.batch, w.max_blocks_per_seq), unused[0], dtype=np.int32)
+    tab[rows, cols] = np.asarray(perm[:needed], dtype=np.int32)
+    tables = torch.from_numpy(tab)
 
     dt = torch_dtype(w.dtype)
     dev = torch.device(device)
@@ -321,20 +325,25 @@ def make_case(w: Workload | str, device="cpu", window: int | None = None,
             else:
                 k.index_fill_(0, ids, nan)
                 v.index_fill_(0, ids, nan)
+        # slots past each sequence's end in its last block, all at once
+        last, slot = [], []
         for b, L in enumerate(lens):
             tail = L % bs
             if tail and used[b]:
-                last = used[b][-1]
-                slots = torch.arange(tail, bs, device=dev)
-                kb = k.view(torch.uint8) if fp8 else k
-                vb = v.view(torch.uint8) if fp8 else v
-                bad = 0x7F if fp8 else nan
-                if tiled:
-                    c, half, j = k_slot(slots)
-                    kb[last, :, c, half, :, j, :] = bad
-                else:
-                    kb[last, :, tail:, :] = bad
-                vb[last, :, slots // g, :, slots % g] = bad
+                last.append(np.full(bs - tail, used[b][-1], dtype=np.int64))
+                slot.append(np.arange(tail, bs, dtype=np.int64))
+        if last:
+            blk = torch.from_numpy(np.concatenate(last)).to(dev)
+            slots = torch.from_numpy(np.concatenate(slot)).to(dev)
+            kb = k.view(torch.uint8) if fp8 else k
+            vb = v.view(torch.uint8) if fp8 else v
+            bad = 0x7F if fp8 else nan
+            if tiled:
+                c, half, j = k_slot(slots)
+                kb[blk, :, c, half, :, j, :] = bad
+            else:
+                kb[blk, :, slots, :] = bad
+            vb[blk, :, slots // g, :, slots % g] = bad
     return Case(
         w=w, window=int(window), q=q, k_cache=k, v_cache=v,
         block_tables=tables.to(dev), seq_lens=torch.tensor(lens, dtype=torch.int32, device=dev),
