@@ -187,6 +187,50 @@ def copy_ceiling(nbytes: int, flush_buf, reps: int = 10) -> dict:
             "gbps": round(moved / us / 1e3, 1), "frac": round(moved / us / 1e3 / PEAK_GBPS, 4)}
 
 
+def read_ceiling(pa, nbytes: int, flush_buf, reps: int = 10) -> dict:
+    """A streaming read of as many HBM bytes as the partition kernel reads
+    (capped at 4 GB) by the library's probe kernel (pa_stream_read: the
+    partition kernels' 16-byte non-temporal loads, coalesced), timed with
+    events around each read and flushed like the calls when they are; the
+    best median over both read patterns and a few grid sizes.  The read rate
+    a plain kernel reaches on this GPU at this size, beside the 8 TB/s peak."""
+    import torch
+    n = max(1, min(nbytes, 4 << 30) // 16) * 4   # int32 elements, whole 16-byte words
+    src = torch.ones(n, dtype=torch.int32, device="cuda")
+    best = None
+    for slab, grid in ((False, 256), (False, 2048), (False, 16384),
+                       (True, 256), (True, 2048), (True, 16384)):
+        sink = torch.zeros(grid, dtype=torch.int32, device="cuda")
+        pa.stream_read(src, sink, slab=slab)
+        ts = []
+        for _ in range(reps):
+            if flush_buf is not None:
+                flush_buf.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            wgs = pa.stream_read(src, sink, slab=slab)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        ts.sort()
+        us = ts[len(ts) // 2]
+        if best is None or us < best[0]:
+            best = (us, wgs, slab)
+    read = 4 * n
+    us, wgs, slab = best
+    del src
+    torch.cuda.empty_cache()
+    return {"kind": "streaming read (pa_stream_read)", "bytes": read, "workgroups": wgs,
+            "pattern": "slab" if slab else "grid stride", "us": round(us, 2),
+            "gbps": round(read / us / 1e3, 1), "frac": round(read / us / 1e3 / PEAK_GBPS, 4)}
+
+
+def with_share(ceiling: dict, achieved_gbps: float) -> dict:
+    """The ceiling record plus the partition kernel's achieved rate as a
+    share of it."""
+    return {**ceiling, "kernel_share": round(achieved_gbps / ceiling["gbps"], 3)}
+
+
 def cpu_model() -> str:
     """CPU model string of this host (from /proc/cpuinfo)."""
     try:
@@ -363,7 +407,11 @@ def side_lines(pa, workloads, main_case, a, flush_buf, reps) -> dict:
         per, kern = timed_reps(call, reps, flush_buf if flush else None)
         nb = algorithmic_bytes(c_win)
         res[f"{name}:w{window}"] = {"flush_between_calls": flush, "plan": call.plan,
-                                    "algorithmic_bytes": nb["total"], **summary(per, kern, nb)}
+                                    "algorithmic_bytes": nb["total"], **summary(per, kern, nb),
+                                    "read_ceiling": None}
+        rc = read_ceiling(pa, nb["partition_kernel"], flush_buf if flush else None)
+        achieved = nb["partition_kernel"] / (res[f"{name}:w{window}"]["kernel_us"]["median"] * 1e-6) / 1e9
+        res[f"{name}:w{window}"]["read_ceiling"] = with_share(rc, achieved)
         del call, c_win
         if c is not main_case:
             del c
@@ -514,6 +562,7 @@ def main(argv=None):
         # with --flush the timed pass also holds one 1 GiB flush read per call
         "ms_per_step_with_flush_reads": round(total_ms / K, 5) if a.flush else None,
         "copy_ceiling": copy_ceiling(nb["partition_kernel"], own_flush),
+        "read_ceiling": with_share(read_ceiling(pa, nb["partition_kernel"], own_flush), achieved),
     }
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(case, out, a.cpu_budget)

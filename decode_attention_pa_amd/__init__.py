@@ -39,7 +39,8 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 EXPORTED_SYMBOLS = (
     "pa_plan_compute", "pa_decode_workspace_size", "pa_decode_workspace_size_ex",
     "pa_decode", "pa_decode_ex", "pa_decode_noalloc", "pa_noalloc_scratch_bytes",
-    "pa_pack_kv_cache", "pa_debug_spans", "pa_check_inputs", "pa_status_string", "pa_last_error",
+    "pa_pack_kv_cache", "pa_debug_spans", "pa_check_inputs", "pa_stream_read", "pa_status_string",
+    "pa_last_error",
 )
 
 
@@ -109,6 +110,7 @@ def load() -> ctypes.CDLL:
     lib.pa_pack_kv_cache.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, P]
     lib.pa_noalloc_scratch_bytes.argtypes = []
     lib.pa_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    lib.pa_stream_read.argtypes = [P, ctypes.c_size_t, P, I32, I32, ctypes.POINTER(I32), P]
     lib.pa_debug_spans.argtypes = [P, P, P, I32, I32, I32, pd, po, P, P, P, P, P]
     lib.pa_check_inputs.argtypes = [P, P, P, I32, I32, I32, pd, P, P]
     lib.pa_status_string.argtypes = [I32]
@@ -117,7 +119,7 @@ def load() -> ctypes.CDLL:
     lib.pa_last_error.restype = ctypes.c_char_p
     for name in ("pa_plan_compute", "pa_decode_workspace_size", "pa_decode_workspace_size_ex",
                  "pa_decode", "pa_decode_ex", "pa_decode_noalloc", "pa_pack_kv_cache",
-                 "pa_debug_spans", "pa_check_inputs"):
+                 "pa_debug_spans", "pa_check_inputs", "pa_stream_read"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -372,6 +374,24 @@ def pack_kv_cache(k_rows, v_rows, k_cache=None, v_cache=None, block_ids=None, st
 def noalloc_scratch_bytes() -> int:
     """Size of the static scratch pa_decode_noalloc uses on each GPU."""
     return int(load().pa_noalloc_scratch_bytes())
+
+
+def stream_read(src, sink, slab=False, stream=None) -> int:
+    """pa_stream_read over the bytes of the contiguous CUDA tensor ``src``
+    into the int32 CUDA tensor ``sink`` (one workgroup per element at most;
+    ``slab``: a contiguous slab per workgroup instead of a grid stride);
+    returns the workgroups launched (the XOR of ``sink[:n]`` is the XOR of
+    every 32-bit word of ``src``)."""
+    import torch
+    if not isinstance(src, torch.Tensor) or src.device.type != "cuda" or not src.is_contiguous():
+        raise PaError(ERR_INVALID_ARG, "src must be a contiguous CUDA tensor")
+    if not isinstance(sink, torch.Tensor) or sink.device.type != "cuda" or sink.dtype != torch.int32:
+        raise PaError(ERR_INVALID_ARG, "sink must be an int32 CUDA tensor")
+    n = ctypes.c_int32(0)
+    _check(load().pa_stream_read(ctypes.c_void_p(src.data_ptr()), _nbytes(src),
+                                 ctypes.c_void_p(sink.data_ptr()), int(sink.numel()),
+                                 1 if slab else 0, ctypes.byref(n), _stream_handle(stream)))
+    return int(n.value)
 
 
 def debug_spans(block_tables, seq_lens, query_lens, window, num_kv_heads, block_size, dims: Dims,

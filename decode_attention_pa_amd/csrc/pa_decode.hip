@@ -16,6 +16,7 @@
 #include "pa_common.h"
 #include "pa_launch.h"
 #include "pa_pack.h"
+#include "pa_probe.h"
 #include "pa_reduce.h"
 #include "pa_valu.h"
 
@@ -756,6 +757,29 @@ pa_status pa_check_inputs(const int32_t* block_tables, const int32_t* seq_lens,
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "check_inputs launch");
+  return PA_OK;
+}
+
+pa_status pa_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t sink_len,
+                         int32_t layout, int32_t* workgroups, void* hip_stream) {
+  if (!src || !sink || !workgroups) return fail(PA_ERR_INVALID_ARG, "a pointer is NULL");
+  if (!aligned(src, 16) || bytes % 16)
+    return fail(PA_ERR_INVALID_ARG, "src must be 16-byte aligned and bytes a multiple of 16");
+  if (!aligned(sink, 4)) return fail(PA_ERR_INVALID_ARG, "sink must be 4-byte aligned");
+  if (sink_len < 1) return fail(PA_ERR_INVALID_ARG, "sink_len %d < 1", sink_len);
+  if (layout != 0 && layout != 1) return fail(PA_ERR_INVALID_ARG, "layout %d unknown", layout);
+  const uint64_t n16 = bytes / 16;
+  const int64_t wgs = std::max<int64_t>(1, std::min<int64_t>(sink_len, cdiv((int64_t)n16, 256)));
+  const hipStream_t s = (hipStream_t)hip_stream;
+  if (layout == 1)
+    hipLaunchKernelGGL(pa::stream_read<true>, dim3((uint32_t)wgs), dim3(256), 0, s,
+                       (const pa::u32x4*)src, n16, sink);
+  else
+    hipLaunchKernelGGL(pa::stream_read<false>, dim3((uint32_t)wgs), dim3(256), 0, s,
+                       (const pa::u32x4*)src, n16, sink);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "stream_read launch");
+  *workgroups = (int32_t)wgs;
   return PA_OK;
 }
 

@@ -335,6 +335,23 @@ pa_status pa_check_inputs(const int32_t* block_tables, const int32_t* seq_lens,
                           int32_t block_size, const pa_dims* dims, int32_t* report,
                           void* hip_stream);
 
+/*
+ * Diagnostic: a streaming read of `bytes` (a multiple of 16) from device
+ * memory at `src` (16-byte aligned), with the same 16-byte non-temporal
+ * loads as the partition kernels, enqueued on `hip_stream`: the HBM read
+ * rate a plain kernel reaches, to set the partition kernels' achieved
+ * bandwidth against.  `layout` 0: the workgroups interleave over the buffer
+ * (grid stride); 1: each reads one contiguous slab.  It launches
+ * min(sink_len, ceil(bytes / 4096)) workgroups of 256 threads (count
+ * returned in *workgroups); workgroup w writes the XOR of the 32-bit words
+ * it read to sink[w] (device memory, 4-byte aligned), so the XOR of
+ * sink[0 .. *workgroups) is the XOR of every word read.  Nothing else is
+ * written.  PA_ERR_INVALID_ARG for NULL pointers, misalignment, an unknown
+ * layout or sink_len < 1.
+ */
+pa_status pa_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t sink_len,
+                         int32_t layout, int32_t* workgroups, void* hip_stream);
+
 /* Static description of a status code. */
 const char* pa_status_string(pa_status status);
 

@@ -385,6 +385,25 @@ def test_check_inputs_rejects_null_pointers(lib):
         assert st == pa.ERR_INVALID_ARG
 
 
+def test_stream_read_rejects_bad_arguments_before_any_launch(lib):
+    """Host-side validation of pa_stream_read (no device touched)."""
+    P = ctypes.c_void_p
+    n = ctypes.c_int32(-7)
+
+    def call(src=P(4096), nbytes=4096, sink=P(1 << 20), sink_len=64, layout=0, wg=ctypes.byref(n)):
+        return lib.pa_stream_read(src, nbytes, sink, sink_len, layout, wg, None)
+
+    assert call(src=None) == pa.ERR_INVALID_ARG
+    assert call(sink=None) == pa.ERR_INVALID_ARG
+    assert call(wg=None) == pa.ERR_INVALID_ARG
+    assert call(src=P(4104)) == pa.ERR_INVALID_ARG        # not 16-byte aligned
+    assert call(nbytes=4100) == pa.ERR_INVALID_ARG        # not whole 16-byte words
+    assert call(sink=P((1 << 20) + 2)) == pa.ERR_INVALID_ARG
+    assert call(sink_len=0) == pa.ERR_INVALID_ARG
+    assert call(layout=2) == pa.ERR_INVALID_ARG
+    assert n.value == -7                                  # nothing launched, nothing written
+
+
 def test_pack_rejects_bad_arguments_before_any_launch(lib):
     """Host-side validation of pa_pack_kv_cache (no device touched)."""
     P = ctypes.c_void_p

@@ -55,3 +55,8 @@ def test_bench_line(args):
         assert cb["cpu_model"] and "threads" in cb["sample"]
     pc = res["per_call"]
     assert pc["reps"] >= 50 and pc["p10"] <= pc["median"] <= pc["p90"]
+    for key in ("copy_ceiling", "read_ceiling"):
+        ce = res[key]
+        assert ce["bytes"] > 0 and ce["us"] > 0 and 0 < ce["frac"] <= 1.05, (key, ce)
+        assert abs(ce["gbps"] - ce["bytes"] / ce["us"] / 1e3) <= 0.1 + 1e-3 * ce["gbps"], (key, ce)
+    assert res["read_ceiling"]["kernel_share"] > 0
