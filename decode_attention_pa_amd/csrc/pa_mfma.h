@@ -207,6 +207,25 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
     }
   }
 
+  // Per tile, the intersection of its real rows' visible intervals
+  // (wave-uniform): a chunk inside it is seen whole by every real row and
+  // needs no mask.  Rows past the sequence's rows do not constrain it: their
+  // scores are never stored.
+  int tlo_all[NRT], thi_all[NRT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    const bool real = r0 + rt * 16 + ln < rows_b;
+    int lo_ = real ? tlo[rt] : INT32_MIN;
+    int hi_ = real ? thi[rt] : INT32_MAX;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      lo_ = max(lo_, __shfl_xor(lo_, off));
+      hi_ = min(hi_, __shfl_xor(hi_, off));
+    }
+    tlo_all[rt] = __builtin_amdgcn_readfirstlane(lo_);
+    thi_all[rt] = __builtin_amdgcn_readfirstlane(hi_);
+  }
+
   auto blocks_of = [&](int k) {
     const int cs = cb0 + k * kChunk;
     const int lo = max(cs, ps);
@@ -278,12 +297,22 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
     }
   };
 
+  // Exp-sums of the rounded weights: at head dims up to 128, one more
+  // matrix-core product per chunk and tile, ones^T P, which sums each row's
+  // weights over the chunk's 32 positions (every lane receives its row's
+  // sum); at 256 (no registers to spare) each lane sums its own 8 weights
+  // and the lane groups are added at the end.
+  constexpr bool LSUM = D <= 128;
+  const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                       (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
   f32x4 o[NRT][DT];
+  f32x4 lacc[NRT];
   float mrun[NRT], lrun[NRT];
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
     mrun[rt] = -INFINITY;
     lrun[rt] = 0.f;
+    lacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -350,11 +379,21 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
             sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(kr[c], 1, s), qf[rt][s], sb, 0, 0, 0);
           }
         }
-        const int p8 = cb0 + (t * CPS + c) * kChunk + 8 * lg;
+        const int cs = cb0 + (t * CPS + c) * kChunk;
+        if (cs >= tlo_all[rt] && cs + kChunk - 1 <= thi_all[rt]) {
+          // every real row sees the whole chunk
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[c][e] = (uint32_t)(p8 + e - tlo[rt]) <= span ? sa[e] * scale_log2 : -INFINITY;
-          x[c][4 + e] = (uint32_t)(p8 + 4 + e - tlo[rt]) <= span ? sb[e] * scale_log2 : -INFINITY;
+          for (int e = 0; e < 4; ++e) {
+            x[c][e] = sa[e] * scale_log2;
+            x[c][4 + e] = sb[e] * scale_log2;
+          }
+        } else {
+          const int p8 = cs + 8 * lg;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[c][e] = (uint32_t)(p8 + e - tlo[rt]) <= span ? sa[e] * scale_log2 : -INFINITY;
+            x[c][4 + e] = (uint32_t)(p8 + 4 + e - tlo[rt]) <= span ? sb[e] * scale_log2 : -INFINITY;
+          }
         }
       }
       float mx;
@@ -376,7 +415,8 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
         // alpha is exactly 1 for rows that keep their reference (never
         // (-inf) - (-inf)), and 0 for a row leaving -inf
         const float alpha = grow ? __builtin_amdgcn_exp2f(mrun[rt] - mx) : 1.f;
-        lrun[rt] *= alpha;
+        if constexpr (LSUM) lacc[rt] *= alpha;
+        else lrun[rt] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[rt][dt] *= alpha;
         mrun[rt] = grow ? mx : mrun[rt];
@@ -389,10 +429,11 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
         for (int e = 0; e < 8; ++e) {
           const __bf16 pe16 = (__bf16)__builtin_amdgcn_exp2f(x[c][e] - mref);
           pb[c][rt][e] = pe16;
-          psum += (float)pe16;  // normalise by the weights PV actually applies
+          // normalise by the weights PV actually applies
+          if constexpr (!LSUM) psum += (float)pe16;
         }
       }
-      lrun[rt] += psum;
+      if constexpr (!LSUM) lrun[rt] += psum;
     }
 #pragma unroll
     for (int c = 0; c < CPS; ++c) load_k(tn * CPS + c, nb[c], kr[c], past || beyond(tn, c));
@@ -453,6 +494,11 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
             o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vr[c][dt]), pb[c][rt], o[rt][dt],
                                                                 0, 0, 0);
       }
+      if constexpr (LSUM) {
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+          lacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[c][rt], lacc[rt], 0, 0, 0);
+      }
     }
     // Request the next V columns only after PV has read these registers
     // (no second register copy of the step).
@@ -465,8 +511,12 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
 
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
-    lrun[rt] += __shfl_xor(lrun[rt], 16);
-    lrun[rt] += __shfl_xor(lrun[rt], 32);
+    if constexpr (LSUM) {
+      lrun[rt] = lacc[rt][0];
+    } else {
+      lrun[rt] += __shfl_xor(lrun[rt], 16);
+      lrun[rt] += __shfl_xor(lrun[rt], 32);
+    }
   }
 
   if constexpr (NW > 1) {
