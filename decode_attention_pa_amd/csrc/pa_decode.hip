@@ -673,9 +673,8 @@ pa_status pa_pack_kv_cache(const void* k_rows, const void* v_rows, void* k_cache
   auto overlap = [bytes](const char* x, const char* y) { return x < y + bytes && y < x + bytes; };
   if (overlap(kr, kc) || overlap(vr, vc) || overlap(kr, vc) || overlap(vr, kc))
     return fail(PA_ERR_INVALID_ARG, "the row-layout and tiled caches must not overlap");
-  const int n = block_ids ? num_ids : num_blocks;
+  const int n = block_ids ? num_ids : num_blocks;  // grid x (up to 2^31 - 1), heads on y
   if (n == 0) return PA_OK;
-  if (n > 65535 * 1024) return fail(PA_ERR_UNSUPPORTED, "%d blocks in one call", n);
   pa::PackArgs a = {};
   a.k_rows = (const uint8_t*)k_rows;
   a.v_rows = (const uint8_t*)v_rows;
@@ -687,7 +686,7 @@ pa_status pa_pack_kv_cache(const void* k_rows, const void* v_rows, void* k_cache
   a.log2_bs = ilog2_exact(block_size);
   a.head_dim = head_dim;
   a.es = es;
-  hipLaunchKernelGGL(pa::pack_kv, dim3(num_kv_heads, n), dim3(256), 0, (hipStream_t)hip_stream, a);
+  hipLaunchKernelGGL(pa::pack_kv, dim3(n, num_kv_heads), dim3(256), 0, (hipStream_t)hip_stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "pack_kv launch");
   return PA_OK;

@@ -49,12 +49,12 @@ __device__ inline void transpose_groups(const uint8_t* src, uint8_t* dst, int bs
   }
 }
 
-// Grid: x = KV head, y = block (or entry of block_ids).  256 threads.
+// Grid: x = block (or entry of block_ids), y = KV head.  256 threads.
 __global__ __launch_bounds__(256) void pack_kv(PackArgs a) {
-  const int h = blockIdx.x;
-  int blk = blockIdx.y;
+  const int h = blockIdx.y;
+  int blk = blockIdx.x;
   if (a.block_ids) {
-    blk = a.block_ids[blockIdx.y];
+    blk = a.block_ids[blockIdx.x];
     if (blk < 0 || blk >= a.num_blocks) return;  // not a block of this cache
   }
   const int bs = 1 << a.log2_bs, D = a.head_dim, es = a.es;

@@ -55,6 +55,7 @@ SHAPES = [
     dict(name="tiny_f32", head_dim=66, block_size=32, max_blocks_per_seq=2),  # fp32, K rows
     dict(name="gqa_bf16", batch=2, head_dim=200, num_q_heads=16, num_kv_heads=8),  # bf16 D=200
     dict(name="gqa_d256_bf16", batch=2),                                # bf16 D=256
+    dict(name="tiny_f32", pool=70000),            # more blocks than 65536 (one grid dimension)
 ]
 
 
