@@ -199,11 +199,21 @@ def _dtype_code(t) -> int:
     raise PaError(ERR_INVALID_ARG, f"unsupported dtype {t.dtype} (float32 or bfloat16)")
 
 
-def _stream_handle(stream):
+def _stream_handle(stream, device=None):
+    """Handle of ``stream``, or of the current stream of ``device`` (default:
+    the current device); a given stream must belong to ``device``."""
     import torch
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(device)
+    elif device is not None and stream.device != torch.device(device):
+        raise PaError(ERR_INVALID_ARG, f"stream is on {stream.device}, the tensors on {device}")
     return ctypes.c_void_p(int(stream.cuda_stream))
+
+
+def _same_device(dev, **tensors):
+    for name, t in tensors.items():
+        if t is not None and t.device != dev:
+            raise PaError(ERR_INVALID_ARG, f"{name} is on {t.device}, the call's tensors on {dev}")
 
 
 def _kv_format(k_cache) -> int:
@@ -236,6 +246,11 @@ def _validate(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, num_
             raise PaError(ERR_INVALID_ARG, f"{name} must be on the GPU")
         if not t.is_contiguous():
             raise PaError(ERR_INVALID_ARG, f"{name} must be contiguous")
+    for name, t in (("out", out), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("block_tables", block_tables), ("seq_lens", seq_lens),
+                    ("query_lens", query_lens)):
+        if t.device != q.device:
+            raise PaError(ERR_INVALID_ARG, f"{name} is on {t.device}, q on {q.device}: one GPU per call")
     for name, t in (("block_tables", block_tables), ("seq_lens", seq_lens), ("query_lens", query_lens)):
         if t.dtype != torch.int32:
             raise PaError(ERR_INVALID_ARG, f"{name} must be int32")
@@ -297,19 +312,21 @@ def decode(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, scale, 
     dims = dims_for(q, k_cache, block_tables, max_query_len, max_seq_len)
     opts = make_options(path, part_size, waves, event_begin, event_end, schedule, loads,
                         k_scale, v_scale, q_scale)
-    need = workspace_size(dims, window, num_kv_heads, block_size, path=path,
-                          part_size=part_size, waves=waves, schedule=schedule)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
-    ws_bytes = _nbytes(workspace) if workspace is not None else 0
-    _check(load().pa_decode_ex(
-        ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(q.data_ptr()),
-        ctypes.c_void_p(k_cache.data_ptr()), ctypes.c_void_p(v_cache.data_ptr()),
-        ctypes.c_void_p(block_tables.data_ptr()), ctypes.c_void_p(seq_lens.data_ptr()),
-        ctypes.c_void_p(query_lens.data_ptr()), ctypes.c_float(scale), int(window),
-        int(num_kv_heads), int(block_size), ctypes.byref(dims), ws_ptr, ws_bytes,
-        _stream_handle(stream), ctypes.byref(opts)))
+    _same_device(q.device, workspace=workspace, k_scale=k_scale, v_scale=v_scale, q_scale=q_scale)
+    with torch.cuda.device(q.device):   # the library sizes its plan for the current device
+        need = workspace_size(dims, window, num_kv_heads, block_size, path=path,
+                              part_size=part_size, waves=waves, schedule=schedule)
+        if workspace is None and need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+        ws_bytes = _nbytes(workspace) if workspace is not None else 0
+        _check(load().pa_decode_ex(
+            ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(q.data_ptr()),
+            ctypes.c_void_p(k_cache.data_ptr()), ctypes.c_void_p(v_cache.data_ptr()),
+            ctypes.c_void_p(block_tables.data_ptr()), ctypes.c_void_p(seq_lens.data_ptr()),
+            ctypes.c_void_p(query_lens.data_ptr()), ctypes.c_float(scale), int(window),
+            int(num_kv_heads), int(block_size), ctypes.byref(dims), ws_ptr, ws_bytes,
+            _stream_handle(stream, q.device), ctypes.byref(opts)))
     return out
 
 
@@ -319,19 +336,22 @@ def decode_noalloc(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens,
                    q_scale=None):
     """Runs pa_decode_noalloc on torch tensors (no workspace: the library's
     static per-GPU scratch holds the partial states); returns ``out``."""
+    import torch
     _validate(out, q, k_cache, v_cache, block_tables, seq_lens, query_lens, num_kv_heads, block_size)
     if q.shape[0] == 0:
         return out          # no query token in the batch: nothing to compute, nothing to call
     dims = dims_for(q, k_cache, block_tables, max_query_len, max_seq_len)
     opts = make_options(path, part_size, waves, None, None, schedule, loads, k_scale, v_scale,
                         q_scale)
-    _check(load().pa_decode_noalloc(
-        ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(q.data_ptr()),
-        ctypes.c_void_p(k_cache.data_ptr()), ctypes.c_void_p(v_cache.data_ptr()),
-        ctypes.c_void_p(block_tables.data_ptr()), ctypes.c_void_p(seq_lens.data_ptr()),
-        ctypes.c_void_p(query_lens.data_ptr()), ctypes.c_float(scale), int(window),
-        int(num_kv_heads), int(block_size), ctypes.byref(dims), _stream_handle(stream),
-        ctypes.byref(opts)))
+    _same_device(q.device, k_scale=k_scale, v_scale=v_scale, q_scale=q_scale)
+    with torch.cuda.device(q.device):   # the scratch used is the current device's
+        _check(load().pa_decode_noalloc(
+            ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(q.data_ptr()),
+            ctypes.c_void_p(k_cache.data_ptr()), ctypes.c_void_p(v_cache.data_ptr()),
+            ctypes.c_void_p(block_tables.data_ptr()), ctypes.c_void_p(seq_lens.data_ptr()),
+            ctypes.c_void_p(query_lens.data_ptr()), ctypes.c_float(scale), int(window),
+            int(num_kv_heads), int(block_size), ctypes.byref(dims), _stream_handle(stream, q.device),
+            ctypes.byref(opts)))
     return out
 
 
@@ -362,12 +382,15 @@ def pack_kv_cache(k_rows, v_rows, k_cache=None, v_cache=None, block_ids=None, st
             raise PaError(ERR_INVALID_ARG, f"{name} must match k_rows in size and dtype")
     if block_ids is not None and (block_ids.dtype != torch.int32 or block_ids.device.type != "cuda"):
         raise PaError(ERR_INVALID_ARG, "block_ids must be an int32 CUDA tensor")
-    _check(load().pa_pack_kv_cache(
-        ctypes.c_void_p(k_rows.data_ptr()), ctypes.c_void_p(v_rows.data_ptr()),
-        ctypes.c_void_p(k_cache.data_ptr()), ctypes.c_void_p(v_cache.data_ptr()),
-        ctypes.c_void_p(block_ids.data_ptr()) if block_ids is not None else None,
-        int(block_ids.numel()) if block_ids is not None else 0, int(nb), int(hkv), int(bs), int(D),
-        int(dtype), KV_FP8_E4M3 if fp8 else KV_NATIVE, _stream_handle(stream)))
+    dev = k_rows.device
+    _same_device(dev, v_rows=v_rows, k_cache=k_cache, v_cache=v_cache, block_ids=block_ids)
+    with torch.cuda.device(dev):
+        _check(load().pa_pack_kv_cache(
+            ctypes.c_void_p(k_rows.data_ptr()), ctypes.c_void_p(v_rows.data_ptr()),
+            ctypes.c_void_p(k_cache.data_ptr()), ctypes.c_void_p(v_cache.data_ptr()),
+            ctypes.c_void_p(block_ids.data_ptr()) if block_ids is not None else None,
+            int(block_ids.numel()) if block_ids is not None else 0, int(nb), int(hkv), int(bs),
+            int(D), int(dtype), KV_FP8_E4M3 if fp8 else KV_NATIVE, _stream_handle(stream, dev)))
     return k_cache, v_cache
 
 
@@ -387,10 +410,13 @@ def stream_read(src, sink, slab=False, stream=None) -> int:
         raise PaError(ERR_INVALID_ARG, "src must be a contiguous CUDA tensor")
     if not isinstance(sink, torch.Tensor) or sink.device.type != "cuda" or sink.dtype != torch.int32:
         raise PaError(ERR_INVALID_ARG, "sink must be an int32 CUDA tensor")
+    _same_device(src.device, sink=sink)
     n = ctypes.c_int32(0)
-    _check(load().pa_stream_read(ctypes.c_void_p(src.data_ptr()), _nbytes(src),
-                                 ctypes.c_void_p(sink.data_ptr()), int(sink.numel()),
-                                 1 if slab else 0, ctypes.byref(n), _stream_handle(stream)))
+    with torch.cuda.device(src.device):
+        _check(load().pa_stream_read(ctypes.c_void_p(src.data_ptr()), _nbytes(src),
+                                     ctypes.c_void_p(sink.data_ptr()), int(sink.numel()),
+                                     1 if slab else 0, ctypes.byref(n),
+                                     _stream_handle(stream, src.device)))
     return int(n.value)
 
 
@@ -406,12 +432,15 @@ def debug_spans(block_tables, seq_lens, query_lens, window, num_kv_heads, block_
     blocks = torch.full((B, dims.max_blocks_per_seq), -7, dtype=torch.int32, device=dev)
     parts = torch.full((B, p["num_parts"], 2), -7, dtype=torch.int32, device=dev)
     o = make_options(**opts)
-    _check(load().pa_debug_spans(
-        ctypes.c_void_p(block_tables.data_ptr()), ctypes.c_void_p(seq_lens.data_ptr()),
-        ctypes.c_void_p(query_lens.data_ptr()), int(window), int(num_kv_heads), int(block_size),
-        ctypes.byref(dims), ctypes.byref(o), ctypes.c_void_p(seq_info.data_ptr()),
-        ctypes.c_void_p(row_info.data_ptr()), ctypes.c_void_p(blocks.data_ptr()),
-        ctypes.c_void_p(parts.data_ptr()), _stream_handle(stream)))
+    _same_device(dev, seq_lens=seq_lens, query_lens=query_lens)
+    with torch.cuda.device(dev):
+        _check(load().pa_debug_spans(
+            ctypes.c_void_p(block_tables.data_ptr()), ctypes.c_void_p(seq_lens.data_ptr()),
+            ctypes.c_void_p(query_lens.data_ptr()), int(window), int(num_kv_heads),
+            int(block_size), ctypes.byref(dims), ctypes.byref(o),
+            ctypes.c_void_p(seq_info.data_ptr()), ctypes.c_void_p(row_info.data_ptr()),
+            ctypes.c_void_p(blocks.data_ptr()), ctypes.c_void_p(parts.data_ptr()),
+            _stream_handle(stream, dev)))
     return dict(seq_info=seq_info, row_info=row_info[:total_q], blocks=blocks, parts=parts, plan=p)
 
 
@@ -434,12 +463,16 @@ class Prepared:
         self.opts = make_options(path, part_size, waves, event_begin, event_end, schedule, loads,
                                  k_scale, v_scale, q_scale)
         self._events = (event_begin, event_end)
+        _same_device(q.device, workspace=workspace, k_scale=k_scale, v_scale=v_scale,
+                     q_scale=q_scale)
+        self._device = q.device.index if q.device.index is not None else torch.cuda.current_device()
         self.plan = plan(self.dims, window, num_kv_heads, block_size,
                          num_cus=torch.cuda.get_device_properties(q.device).multi_processor_count,
                          path=path, part_size=part_size, waves=waves, schedule=schedule,
                          loads=loads)
-        need = workspace_size(self.dims, window, num_kv_heads, block_size, path=path,
-                              part_size=part_size, waves=waves, schedule=schedule)
+        with torch.cuda.device(q.device):
+            need = workspace_size(self.dims, window, num_kv_heads, block_size, path=path,
+                                  part_size=part_size, waves=waves, schedule=schedule)
         if workspace is None and need:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         self.workspace = workspace
@@ -454,7 +487,7 @@ class Prepared:
             ctypes.byref(self.dims),
             vp(workspace.data_ptr()) if workspace is not None else None,
             _nbytes(workspace) if workspace is not None else 0,
-            _stream_handle(stream), ctypes.byref(self.opts))
+            _stream_handle(stream, q.device), ctypes.byref(self.opts))
         self._fn = load().pa_decode_ex
 
     def set_events(self, event_begin, event_end):
@@ -468,7 +501,12 @@ class Prepared:
     def __call__(self):
         if self._empty:
             return          # no query token in the batch
-        st = self._fn(*self.args)
+        import torch
+        if torch.cuda.current_device() != self._device:
+            with torch.cuda.device(self._device):
+                st = self._fn(*self.args)
+        else:
+            st = self._fn(*self.args)
         if st:
             _check(st)
 
@@ -478,13 +516,16 @@ def check_inputs(block_tables, seq_lens, query_lens, window, num_kv_heads, block
     """Device-side precondition report of a call's lengths and block tables
     (see pa_check_inputs); waits for the stream."""
     import torch
-    report = torch.empty(4, dtype=torch.int32, device=block_tables.device)
-    s = _stream_handle(stream)
-    _check(load().pa_check_inputs(
-        ctypes.c_void_p(block_tables.data_ptr()), ctypes.c_void_p(seq_lens.data_ptr()),
-        ctypes.c_void_p(query_lens.data_ptr()), int(window), int(num_kv_heads), int(block_size),
-        ctypes.byref(dims), ctypes.c_void_p(report.data_ptr()), s))
-    (stream or torch.cuda.current_stream()).synchronize()
+    dev = block_tables.device
+    _same_device(dev, seq_lens=seq_lens, query_lens=query_lens)
+    report = torch.empty(4, dtype=torch.int32, device=dev)
+    with torch.cuda.device(dev):
+        s = _stream_handle(stream, dev)
+        _check(load().pa_check_inputs(
+            ctypes.c_void_p(block_tables.data_ptr()), ctypes.c_void_p(seq_lens.data_ptr()),
+            ctypes.c_void_p(query_lens.data_ptr()), int(window), int(num_kv_heads),
+            int(block_size), ctypes.byref(dims), ctypes.c_void_p(report.data_ptr()), s))
+    (stream or torch.cuda.current_stream(dev)).synchronize()
     r = report.cpu().tolist()
     none = 0x7fffffff
     return dict(bad_lengths=r[0], bad_entries=r[1],

@@ -439,3 +439,22 @@ def test_large_batches_scan_row_offsets(lib):
     states = 5000 * 8 * split["num_parts"] * split["rows"]
     assert split["workspace_bytes"] == (2 * al(4 * states) + al(4 * states * 128)
                                         + al(4 * 5000))
+
+
+def test_binding_rejects_tensors_and_streams_of_another_device():
+    """The binding keeps one call on one GPU: a tensor or a stream on another
+    device than the call's tensors is refused before the library is called."""
+    import torch
+    with pytest.raises(pa.PaError) as e:
+        pa._same_device(torch.device("cuda", 0), workspace=torch.empty(4))
+    assert e.value.status == pa.ERR_INVALID_ARG and "workspace" in str(e.value)
+    pa._same_device(torch.device("cpu"), workspace=torch.empty(4), k_scale=None)
+
+    class FakeStream:
+        device = torch.device("cuda", 1)
+        cuda_stream = 0
+
+    with pytest.raises(pa.PaError) as e:
+        pa._stream_handle(FakeStream(), torch.device("cuda", 0))
+    assert e.value.status == pa.ERR_INVALID_ARG
+    assert pa._stream_handle(FakeStream(), torch.device("cuda", 1)).value is None
