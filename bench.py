@@ -446,6 +446,9 @@ def main(argv=None):
                     help="(no GPU) record rocprofv3 FETCH_SIZE/WRITE_SIZE runs of this "
                          "workload into profiles/traffic.json and exit")
     ap.add_argument("--ingest-command", default="", help="command line that produced them")
+    ap.add_argument("--context", type=int, default=0,
+                    help="every sequence of the workload this many positions long instead of "
+                         "the workload's lengths (a context sweep; no traffic record applies)")
     a = ap.parse_args(argv)
     if a.ingest_counters:
         w = a.workload
@@ -467,6 +470,12 @@ def main(argv=None):
         return 1
     torch.cuda.set_device(0)
     w = workloads.WORKLOADS[a.workload]
+    if a.context:
+        if a.context < w.query_len:
+            print(f"--context {a.context} is shorter than the query length {w.query_len}",
+                  file=sys.stderr)
+            return 2
+        w = workloads.with_context(w, a.context)
     window = w.windows[0] if a.window is None else a.window
     case = workloads.make_case(w, device="cuda", window=window)
     call = make_call(pa, case, window, a)
@@ -524,7 +533,7 @@ def main(argv=None):
     us_per_call = (sum(flushed_ms) / K if a.flush else total_ms / K) * 1e3
     achieved = nb["partition_kernel"] / (kern_avg * 1e-6) / 1e9
     call_gbps = nb["total"] / (us_per_call * 1e-6) / 1e9
-    traffic = load_traffic(a.workload, window)
+    traffic = None if a.context else load_traffic(a.workload, window)
     stats = summary(per, kern, nb)
 
     res = {
@@ -547,6 +556,7 @@ def main(argv=None):
             "kv_dtype": w.kv_dtype or w.dtype, "q_dtype": w.q_dtype or w.dtype,
             "realised_context_tokens": sum(case.seq_lens_host), "plan": call.plan,
             "flush_between_calls": bool(a.flush),
+            "context_override": a.context or None,
         },
         "achieved_gbps_per_call": round(call_gbps, 1),
         "frac_of_peak_per_call": round(call_gbps / PEAK_GBPS, 4),

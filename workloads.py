@@ -356,6 +356,14 @@ def make_case(w: Workload | str, device="cpu", window: int | None = None,
         if w.q_dtype == "fp8" else None)
 
 
+def with_context(w: Workload, L: int) -> Workload:
+    """``w`` with every sequence exactly ``L`` positions long (its block
+    tables sized for that, a fresh pool)."""
+    return replace(w, seq_lens=(int(L),) * w.batch, len_range=(), max_seq_len=int(L),
+                   max_blocks_per_seq=-(-int(L) // w.block_size) + 1, pool=0,
+                   query_lens=())
+
+
 def custom(name="custom", **kw) -> Workload:
     """A workload built from keyword overrides of the tiny fp32 one."""
     base = WORKLOADS["tiny_f32"]
