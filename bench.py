@@ -53,7 +53,8 @@ def kernel_source_hash() -> str:
     from decode_attention_pa_amd import build as b
     d = os.path.join(ROOT, "decode_attention_pa_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("pa_common.h", "pa_mfma.h", "pa_valu.h", "pa_wave.h", "pa_launch.h", "pa_decode.hip",
+    for f in ("pa_common.h", "pa_sched.h", "pa_mfma.h", "pa_valu.h", "pa_wave.h", "pa_launch.h",
+              "pa_decode.hip",
               "pa_mfma_d64.hip", "pa_mfma_d128.hip", "pa_mfma_d256.hip", "pa_wave_kernels.hip"):
         src = open(os.path.join(d, f), encoding="utf-8").read()
         if f == "pa_decode.hip":

@@ -88,6 +88,15 @@ uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 // batches of prefill chunks and decode rows, in blocks of 16 to 64 rows.
 constexpr int kMaxRows = 1024;
 
+// Register-resident vector kernels on the persistent schedule: whether
+// automatic plans take it (as on the matrix cores), and the workgroups per
+// CU its grid may hold; the launcher caps them at what fits (3 at head dim
+// 128).  Measured on MI355X: the fp32 GQA batch 214-219 -> 202 us (kernel)
+// with every resident workgroup, 204 with 2 per CU, 227 with 1; the bf16
+// GQA batch on the vector kernel 140 -> 126 us.
+constexpr bool kWavePersistentAuto = true;
+constexpr int kWavePsPerCu = 8;
+
 // Head dims with matrix-core kernels (whole 32-dim k-steps, instantiated).
 bool mfma_head_dim(int D) { return D == 64 || D == 128 || D == 256; }
 
@@ -229,8 +238,9 @@ pa_status make_plan(const pa_dims* d, int32_t window, int32_t hkv, int32_t bs, i
   const int sched_req = o ? o->schedule : 0;
   if (sched_req < 0 || sched_req > 2) return fail(PA_ERR_INVALID_ARG, "schedule %d unknown", sched_req);
   if (sched_req == 2) {
-    if (r.path != PA_PATH_MFMA)
-      return fail(PA_ERR_UNSUPPORTED, "the persistent schedule needs the matrix-core path");
+    if (r.path != PA_PATH_MFMA && r.path != PA_PATH_VALU)
+      return fail(PA_ERR_UNSUPPORTED,
+                  "the persistent schedule needs the matrix-core or register-resident vector path");
     if (d->batch > pa::kPsMaxBatch)
       return fail(PA_ERR_UNSUPPORTED, "the persistent schedule handles batch <= %d", pa::kPsMaxBatch);
     if (r.row_blocks > 1)
@@ -238,9 +248,11 @@ pa_status make_plan(const pa_dims* d, int32_t window, int32_t hkv, int32_t bs, i
   }
   // Persistent schedule (measured on MI355X: +3-5 % on many-unit split
   // shapes, slightly slower for one (sequence, head) or one-shot calls):
-  // matrix-core path, at least 64 (sequence, KV head) units, batch that fits
-  // its shared-memory prefix sums, and a span long enough to split.
-  const bool ps_auto = r.path == PA_PATH_MFMA && units >= 64 && d->batch <= pa::kPsMaxBatch &&
+  // matrix-core or register-resident vector path, at least 64 (sequence, KV
+  // head) units, batch that fits its shared-memory prefix sums, a span long
+  // enough to split, and every row of a unit in one workgroup.
+  const bool ps_path = r.path == PA_PATH_MFMA || (r.path == PA_PATH_VALU && kWavePersistentAuto);
+  const bool ps_auto = ps_path && units >= 64 && d->batch <= pa::kPsMaxBatch &&
                        span_cover > 8 * pa::kChunk && r.row_blocks == 1;
   r.persistent = sched_req == 2 ? 1 : (sched_req == 1 ? 0 : (ps_auto ? 1 : 0));
   const int p_req = o ? o->part_size : 0;
@@ -335,7 +347,9 @@ pa_status make_plan(const pa_dims* d, int32_t window, int32_t hkv, int32_t bs, i
   r.ps_grid = 0;
   if (r.persistent) {
     const bool kv8 = d->kv_format == PA_KV_FP8_E4M3;
-    r.ps_grid = pa::ps_wgs_per_cu(d->head_dim, r.row_tiles, r.waves, kv8) * num_cus;
+    r.ps_grid = (r.path == PA_PATH_VALU ? kWavePsPerCu
+                                        : pa::ps_wgs_per_cu(d->head_dim, r.row_tiles, r.waves, kv8)) *
+                num_cus;
   }
   r.workspace_bytes = workspace_layout(r, *d, hkv).total;
   *p = r;
@@ -473,7 +487,8 @@ pa_status run(void* out, const void* q, const void* k_cache, const void* v_cache
       default: ok = pa_host::launch_mfma_256(nrt, p.waves, grid, p.persistent, p.streaming, kv8, q8, cus, L, a); break;
     }
   } else if (p.path == PA_PATH_VALU) {
-    ok = pa_host::launch_wave(d->dtype == PA_F32, d->head_dim, p.block_rows, grid, L, a);
+    ok = pa_host::launch_wave(d->dtype == PA_F32, d->head_dim, p.block_rows, grid, p.persistent,
+                              cus, L, a);
   } else if (d->dtype == PA_F32) {
     launch_part(pa::part_valu<float>, grid, dim3(256), L, a);
   } else {

@@ -96,7 +96,9 @@ bool launch_mfma_256(int nrt, int nw, dim3 grid, bool persistent, bool streaming
                      int cus, const Launch& L, const pa::PartArgs& a);
 
 // Register-resident vector kernels (pa_wave_kernels.hip): fp32 or bf16
-// caches, head dims 64, 128 and 256, 4 or 8 rows per workgroup.
-bool launch_wave(bool f32, int D, int block_rows, dim3 grid, const Launch& L, const pa::PartArgs& a);
+// caches, head dims 64, 128 and 256, 4 or 8 rows per workgroup, grid or
+// persistent schedule.
+bool launch_wave(bool f32, int D, int block_rows, dim3 grid, bool persistent, int cus,
+                 const Launch& L, const pa::PartArgs& a);
 
 }  // namespace pa_host

@@ -40,6 +40,7 @@
 #include <type_traits>
 
 #include "pa_common.h"
+#include "pa_sched.h"
 
 namespace pa {
 
@@ -107,10 +108,6 @@ __host__ __device__ constexpr int ps_wgs_per_cu(int D, int NRT, int NW, bool kv8
                          ? 65536 / (NW * kChunk * 2 * D * (kv8 ? 1 : 2)) : 1)
                   : (16 / NW > 1 ? 16 / NW : 1);
 }
-
-// Largest batch the persistent schedule handles (its per-sequence prefix sums
-// live in shared memory); larger batches use the grid schedule.
-constexpr int kPsMaxBatch = 1024;
 
 struct ChunkBlocks {
   int first_idx;  // logical block index of the first in-partition position
@@ -612,111 +609,13 @@ __global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
                                                sv.nparts == 1, r0);
 }
 
-// Persistent schedule (aiter PR #2914: "PS" decode): a grid whose
-// workgroups are all resident at once (the launcher picks how many per CU,
-// at most what fits).  The partitions of all units form one list,
-// unit-major ((sequence, KV head), then partition); workgroup w takes the
-// contiguous share [w*I/W, (w+1)*I/W) of the I partitions and runs each
-// unit's stretch of it as one run.  Shares differ by at most one partition,
-// so there is no tail of late workgroups, and a workgroup's set-up is paid
-// once per unit it touches rather than once per partition.  A run that is a
-// whole unit writes `out`; otherwise it stores its state in slot w + u (w
-// its workgroup, u = b * H_kv + h its unit).  Walking the shares in order,
-// each (share, unit) pair steps w, u or both up by one, so these slots are
-// distinct, those of one unit are consecutive (w_first + u onwards), and
-// all lie below W + units: the workspace holds W + units states, whatever
-// the partition count.  The unit's last run records its run count and first
-// slot for the merge (count 0 when the unit was written directly).
+// Persistent schedule (persistent_shares in pa_sched.h) on the matrix cores.
 template <int D, int NRT, int NW, bool STREAM, bool KV8, bool Q8>
 __global__ __launch_bounds__(64 * NW) void part_mfma_ps(PartArgs a) {
-  constexpr int NT = 64 * NW;
-  __shared__ int s_np[kPsMaxBatch + 1];  // exclusive prefix of partitions per sequence
-  __shared__ int s_q[kPsMaxBatch + 1];   // exclusive prefix of query tokens (q/out row)
-  __shared__ int s_wave[2][NW];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int B = a.batch;
-  // Block-wide exclusive scan of (partitions, query tokens) over sequences.
-  const int per = (B + NT - 1) / NT;
-  const int k0 = min(B, tid * per), k1 = min(B, k0 + per);
-  int cnt_np = 0, cnt_q = 0;
-  for (int k = k0; k < k1; ++k) {
-    const int q = a.query_lens[k];
-    cnt_np += seq_view(a.seq_lens[k], q, a.window, a.part_size).nparts;
-    cnt_q += q;
-  }
-  int inc_np = cnt_np, inc_q = cnt_q;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int t_np = __shfl_up(inc_np, off), t_q = __shfl_up(inc_q, off);
-    if (lane >= off) {
-      inc_np += t_np;
-      inc_q += t_q;
-    }
-  }
-  if (lane == 63) {
-    s_wave[0][wave] = inc_np;
-    s_wave[1][wave] = inc_q;
-  }
-  __syncthreads();
-  int run_np = inc_np - cnt_np, run_q = inc_q - cnt_q;
-  for (int w = 0; w < wave; ++w) {
-    run_np += s_wave[0][w];
-    run_q += s_wave[1][w];
-  }
-  for (int k = k0; k < k1; ++k) {
-    s_np[k] = run_np;
-    s_q[k] = run_q;
-    const int q = a.query_lens[k];
-    run_np += seq_view(a.seq_lens[k], q, a.window, a.part_size).nparts;
-    run_q += q;
-  }
-  if (tid == NT - 1) {
-    s_np[B] = run_np;
-    s_q[B] = run_q;
-  }
-  __syncthreads();
-
-  const int H = a.num_kv_heads;
-  const long total = (long)H * s_np[B];
-  // Shares over at most `total` workgroups, so that every share is non-empty
-  // and a run's ordinal within its unit stays below the unit's partition count.
-  const long W = min((long)gridDim.x, total);
-  if ((long)blockIdx.x >= W) return;
-  long i0 = (long)blockIdx.x * total / W;
-  const long i1 = ((long)blockIdx.x + 1) * total / W;
-  while (i0 < i1) {
-    // sequence of partition i0: the last b with H * s_np[b] <= i0
-    int lo = 0, hi = B - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if ((long)H * s_np[mid] <= i0) lo = mid;
-      else hi = mid - 1;
-    }
-    const int b = __builtin_amdgcn_readfirstlane(lo);
-    const int np_b = s_np[b + 1] - s_np[b];
-    const long rel = i0 - (long)H * s_np[b];
-    const int h = __builtin_amdgcn_readfirstlane((int)(rel / np_b));
-    const int j1 = __builtin_amdgcn_readfirstlane((int)(rel - (long)h * np_b));
-    const int j2 = (int)min((long)np_b - 1, (long)j1 + (i1 - i0) - 1);
-    const int L = a.seq_lens[b];
-    const int q = a.query_lens[b];
-    const SeqView sv = seq_view(L, q, a.window, a.part_size);
-    // ordinal of this run among the unit's runs: this workgroup minus the
-    // workgroup whose share holds the unit's first partition (item A);
-    // share w starts at floor(w*I/W), so item i lies in share ceil((i+1)W/I)-1
-    const long A = (long)H * s_np[b] + (long)h * np_b;
-    const long w_first = ((A + 1) * W + total - 1) / total - 1;
-    const int slot = (int)((long)blockIdx.x - w_first);
-    const bool whole = (j1 == 0 && j2 == np_b - 1);
-    const size_t unit = (size_t)b * H + h;
-    mfma_run<D, NRT, NW, STREAM, KV8, Q8, true>(a, b, h, L, q, s_q[b], sv, j1, j2,
-                                              (size_t)blockIdx.x + unit, whole);
-    // (one-shot plans have no workspace: every unit is whole and no merge runs)
-    if (j2 == np_b - 1 && tid == 0 && a.ws_runs != nullptr)
-      *(int2*)(a.ws_runs + 2 * unit) = make_int2(whole ? 0 : slot + 1, (int)(w_first + (long)unit));
-    __syncthreads();  // the next run reuses the merge's shared memory
-    i0 += j2 - j1 + 1;
-  }
+  persistent_shares<64 * NW>(a, [&](int b, int h, int L, int q, int qoff, const SeqView& sv, int j1,
+                                    int j2, size_t state, bool whole) {
+    mfma_run<D, NRT, NW, STREAM, KV8, Q8, true>(a, b, h, L, q, qoff, sv, j1, j2, state, whole);
+  });
 }
 
 }  // namespace pa

@@ -32,6 +32,7 @@
 #pragma once
 
 #include "pa_common.h"
+#include "pa_sched.h"
 #include "pa_valu.h"
 
 namespace pa {
@@ -133,8 +134,16 @@ __device__ __forceinline__ void dot8<8, 8>(float (&s)[8], const float (&q)[8], c
 #undef PA_ROWS4
 #undef PA_FMA
 
+// One run: partitions j_first .. j_last of unit (sequence b, KV head h),
+// rows r0 .. r0 + RB - 1 of it, as one stretch of positions taken by the 4
+// waves in steps of 64.  With `write_out` (the run is the whole unit) it
+// writes `out`; otherwise its state (max, exp-sum, normalised output) goes
+// to state slot `state` (R rows per slot).  All waves of the workgroup call
+// it with the same arguments, and all return from it.
 template <typename T, int D, int RB>
-__global__ __launch_bounds__(256) void part_wave(PartArgs a) {
+__device__ __forceinline__ void wave_run(const PartArgs& a, int b, int h, int L, int q, int qoff,
+                                         const SeqView& sv, int j_first, int j_last, size_t state,
+                                         bool write_out, int r0) {
   constexpr int NW = 4;
   constexpr int DL = D / 64;  // output dims per lane
   constexpr int NJ = D / 16;  // 16-dim slices of a key
@@ -146,21 +155,13 @@ __global__ __launch_bounds__(256) void part_wave(PartArgs a) {
   __shared__ float m_s[NW][RB], l_s[NW][RB];
   __shared__ float o_s[NW - 1][RB][D];
 
-  const PartItem it = part_item(a);
-  const int j = it.j, h = it.h, b = it.b;
-  const int L = a.seq_lens[b];
-  const int q = a.query_lens[b];
-  const SeqView sv = seq_view(L, q, a.window, a.part_size);
-  if (j >= sv.nparts) return;  // empty partition: contributes nothing
+  qoff = __builtin_amdgcn_readfirstlane(qoff);  // uniform: addresses stay scalar
   const int G = a.group;
   const int rows_b = G * q;
-  const int r0 = it.rb * RB;
-  if (r0 >= rows_b) return;    // no row of this sequence in this block
-  int ps, pe;
-  partition_range(sv, j, a.part_size, &ps, &pe);
-  const int cb0 = sv.base + j * a.part_size;  // multiple of 32
+  const int ps = max(sv.lo, sv.base + j_first * a.part_size);
+  const int pe = min(sv.hi, sv.base + (j_last + 1) * a.part_size);
+  const int cb0 = sv.base + j_first * a.part_size;  // multiple of 32
   const int nst = (pe - cb0 + 63) / 64;
-  const int qoff = __builtin_amdgcn_readfirstlane(row_offset(a.qoffs, a.query_lens, b));
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int log2_bs = a.log2_bs;
@@ -312,9 +313,9 @@ __global__ __launch_bounds__(256) void part_wave(PartArgs a) {
       for (int dl = 0; dl < DL; ++dl) o_s[wave - 1][r][lane * DL + dl] = acc[r][dl];
   }
   __syncthreads();
-  if (wave != 0) return;
-  const bool one_shot = (sv.nparts == 1);
-  const size_t wbase = (((size_t)b * a.num_kv_heads + h) * a.num_parts + j) * a.rows;
+  if (wave != 0) return;  // (every wave returns; wave 0 after the stores below)
+  const bool one_shot = write_out;
+  const size_t wbase = state * a.rows;
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
     const int n = r0 + r;
@@ -351,6 +352,31 @@ __global__ __launch_bounds__(256) void part_wave(PartArgs a) {
       }
     }
   }
+}
+
+// Grid schedule: one workgroup per (partition, sequence, KV head, row block).
+template <typename T, int D, int RB>
+__global__ __launch_bounds__(256) void part_wave(PartArgs a) {
+  const PartItem it = part_item(a);
+  const int L = a.seq_lens[it.b];
+  const int q = a.query_lens[it.b];
+  const SeqView sv = seq_view(L, q, a.window, a.part_size);
+  if (it.j >= sv.nparts) return;         // empty partition: contributes nothing
+  const int r0 = it.rb * RB;
+  if (r0 >= a.group * q) return;         // no row of this sequence in this block
+  const int qoff = __builtin_amdgcn_readfirstlane(row_offset(a.qoffs, a.query_lens, it.b));
+  const size_t state = ((size_t)it.b * a.num_kv_heads + it.h) * a.num_parts + it.j;
+  wave_run<T, D, RB>(a, it.b, it.h, L, q, qoff, sv, it.j, it.j, state, sv.nparts == 1, r0);
+}
+
+// Persistent schedule (persistent_shares): every row of a unit in one
+// workgroup (RB >= R).
+template <typename T, int D, int RB>
+__global__ __launch_bounds__(256) void part_wave_ps(PartArgs a) {
+  persistent_shares<256>(a, [&](int b, int h, int L, int q, int qoff, const SeqView& sv, int j1,
+                                int j2, size_t state, bool whole) {
+    wave_run<T, D, RB>(a, b, h, L, q, qoff, sv, j1, j2, state, whole, 0);
+  });
 }
 
 }  // namespace pa

@@ -204,8 +204,16 @@ def test_persistent_schedule_choice(lib):
     assert pa.plan(dims_of(long), 0, 1, 16)["persistent"] == 0         # one unit
     assert pa.plan(dims_of(long), 0, 1, 16, schedule=pa.SCHED_PERSISTENT)["persistent"] == 1
     tiny = workloads.WORKLOADS["tiny_f32"]
-    with pytest.raises(pa.PaError) as e:                              # vector path: grid only
-        pa.plan(dims_of(tiny), 0, 1, 16, schedule=pa.SCHED_PERSISTENT)
+    # register-resident vector path: persistent when asked for (R <= 8 rows in
+    # one workgroup); the staged vector kernel has the grid schedule only
+    p = pa.plan(dims_of(tiny), 0, 1, 16, schedule=pa.SCHED_PERSISTENT)
+    assert p["path"] == pa.PATH_VALU and p["persistent"] == 1 and p["ps_grid"] == 8 * 256
+    assert pa.plan(dims_of(tiny), 0, 1, 16)["persistent"] == 0
+    with pytest.raises(pa.PaError) as e:
+        pa.plan(dims_of(tiny), 0, 1, 16, schedule=pa.SCHED_PERSISTENT, path=pa.PATH_VALU_LDS)
+    assert e.value.status == pa.ERR_UNSUPPORTED
+    with pytest.raises(pa.PaError) as e:                              # 16 rows in 2 blocks of 8
+        pa.plan(dims_of(tiny, num_q_heads=16), 0, 1, 16, schedule=pa.SCHED_PERSISTENT)
     assert e.value.status == pa.ERR_UNSUPPORTED
     with pytest.raises(pa.PaError) as e:
         pa.plan(dims_of(gqa, batch=1025, max_blocks_per_seq=512), 0, 8, 16,

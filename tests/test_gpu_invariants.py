@@ -34,7 +34,8 @@ pytestmark = pytest.mark.gpu
 
 PATHS = [pa.PATH_MFMA, pa.PATH_VALU, pa.PATH_VALU_LDS]
 KERNELS = [(pa.PATH_MFMA, pa.SCHED_GRID), (pa.PATH_MFMA, pa.SCHED_PERSISTENT),
-           (pa.PATH_VALU, pa.SCHED_GRID), (pa.PATH_VALU_LDS, pa.SCHED_GRID)]
+           (pa.PATH_VALU, pa.SCHED_GRID), (pa.PATH_VALU, pa.SCHED_PERSISTENT),
+           (pa.PATH_VALU_LDS, pa.SCHED_GRID)]
 
 
 @pytest.fixture(autouse=True)
