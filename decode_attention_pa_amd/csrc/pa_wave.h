@@ -19,11 +19,13 @@
 //         (xor butterfly); the reference max moves only when a step beats it
 //         by more than 2^8 (as on the matrix cores); a row with nothing
 //         visible keeps -inf and never evaluates (-inf) - (-inf).
-//   PV    lane t owns D/64 consecutive output dims of every row; for each
-//         group of 8 positions it loads those dims' 8-slot runs of the V tile
-//         (16-byte loads) and accumulates p * v, the step's weights read back
-//         as broadcasts from a per-wave shared-memory row (written once per
-//         step, read once per position).
+//   PV    for each group of 8 positions the wave reads the group's [D][8] V
+//         tile as 16-byte columns, lane t taking columns t, t + 64, ... (each
+//         load instruction reads 1 KB contiguous, non-temporal): in bf16 a
+//         column is one dim's 8 slots, in fp32 half of them (a lane pair
+//         shares a dim and adds its halves at the end).  It accumulates
+//         p * v, the step's weights read back from a per-wave shared-memory
+//         row (written once per step).
 //
 // The waves' states are merged in a fixed order at the end (deterministic).
 // Output contract as the other partition kernels: a sequence with one
@@ -52,8 +54,10 @@ __device__ inline float wave_sum(float x) {
 // 8 consecutive elements at p as fp32 (16-byte loads).
 template <typename T>
 __device__ inline void load8(const T* p, float (&x)[8]);
-// Cached 16-byte loads (measured on MI355X: non-temporal ones made the fp32
-// GQA batch 36 % slower on this kernel).
+// Cached 16-byte loads, for K: a key instruction uses half of each line it
+// touches and the next one the other half, so the lines must stay cached
+// (measured on MI355X: non-temporal K loads made the fp32 GQA batch 36 %
+// slower).
 template <typename V>
 __device__ inline V ld16(const V* p) {
   return *p;
@@ -70,6 +74,28 @@ __device__ inline void load8<float>(const float* p, float (&x)[8]) {
 template <>
 __device__ inline void load8<uint16_t>(const uint16_t* p, float (&x)[8]) {
   const u32x4 w = ld16((const u32x4*)p);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = __uint_as_float(w[e] << 16);
+    x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+  }
+}
+
+// One 16-byte column of a V tile as fp32: 4 fp32 or 8 bf16 elements.  V
+// instructions read whole lines (1 KB contiguous per instruction), so they
+// stream past the caches (measured on MI355X, against cached loads: the
+// fp32 GQA batch 202.5 -> 184 us, the bf16 one on this kernel 126 -> 112 us).
+template <typename T>
+__device__ inline void load_col(const T* p, float (&x)[16 / sizeof(T)]);
+template <>
+__device__ inline void load_col<float>(const float* p, float (&x)[4]) {
+  const f32x4 a = __builtin_nontemporal_load((const f32x4*)p);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = a[e];
+}
+template <>
+__device__ inline void load_col<uint16_t>(const uint16_t* p, float (&x)[8]) {
+  const u32x4 w = __builtin_nontemporal_load((const u32x4*)p);
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     x[2 * e] = __uint_as_float(w[e] << 16);
@@ -145,7 +171,14 @@ __device__ __forceinline__ void wave_run(const PartArgs& a, int b, int h, int L,
                                          const SeqView& sv, int j_first, int j_last, size_t state,
                                          bool write_out, int r0) {
   constexpr int NW = 4;
-  constexpr int DL = D / 64;  // output dims per lane
+  // PV reads the [D][8] V tile of a group of 8 positions as 16-byte columns,
+  // column c = 64 * i + lane (i < VC), so that each load instruction reads
+  // 1 KB contiguous.  Column c holds EPC consecutive slots of dim
+  // c * EPC / 8 from slot c * EPC % 8: in bf16 a whole dim (lane owns dims
+  // lane + 64 i), in fp32 half of one (lanes 2m and 2m + 1 share dims
+  // m + 32 i, each summing 4 of the 8 positions, added at the end).
+  constexpr int EPC = 16 / (int)sizeof(T);
+  constexpr int VC = D * 8 / EPC / 64;
   constexpr int NJ = D / 16;  // 16-dim slices of a key
   // Loads in flight per wave: JB 16-element key slices per batch, V groups
   // of 8 positions 4 at a time (measured on MI355X, fp32 GQA batch: 4 and 4
@@ -197,13 +230,15 @@ __device__ __forceinline__ void wave_run(const PartArgs& a, int b, int h, int L,
   }
 
 
-  float mrun[RB], lrun[RB], acc[RB][DL];
+  const int slot0 = (lane * EPC) & 7;  // first slot of this lane's columns
+  auto vdim = [&](int i) { return ((64 * i + lane) * EPC) >> 3; };
+  float mrun[RB], lrun[RB], acc[RB][VC];
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
     mrun[r] = -INFINITY;
     lrun[r] = 0.f;
 #pragma unroll
-    for (int dl = 0; dl < DL; ++dl) acc[r][dl] = 0.f;
+    for (int i = 0; i < VC; ++i) acc[r][i] = 0.f;
   }
 
   for (int t = wave; t < nst; t += NW) {
@@ -252,7 +287,7 @@ __device__ __forceinline__ void wave_run(const PartArgs& a, int b, int h, int L,
         const float alpha = __builtin_amdgcn_exp2f(mrun[r] - mx);  // 0 while mrun = -inf
         lrun[r] *= alpha;
 #pragma unroll
-        for (int dl = 0; dl < DL; ++dl) acc[r][dl] *= alpha;
+        for (int i = 0; i < VC; ++i) acc[r][i] *= alpha;
         mrun[r] = mx;
       }
       const float mref = (mrun[r] == -INFINITY) ? 0.f : mrun[r];
@@ -261,44 +296,51 @@ __device__ __forceinline__ void wave_run(const PartArgs& a, int b, int h, int L,
       p_s[wave][lane][r] = p;
     }
     __builtin_amdgcn_wave_barrier();
-    // PV: lane = DL output dims; 8 groups of 8 positions
+    // PV: lane = VC columns of each group's V tile; 8 groups of 8 positions
 #pragma unroll 4
     for (int gi = 0; gi < 8; ++gi) {
       const int p8 = cs + 8 * gi;
       if (p8 >= pe || p8 + 8 <= ps) continue;  // wave-uniform: the group holds nothing visible
       const int pb = max(p8, ps);
       const int gblk = stable[pb >> log2_bs];
-      const T* vp = vc + (size_t)gblk * blk_stride + head_off + (size_t)((p8 & bs_mask) >> 3) * D * 8 +
-                    (size_t)lane * DL * 8;
-      float v[DL][8];
+      const T* vt = vc + (size_t)gblk * blk_stride + head_off + (size_t)((p8 & bs_mask) >> 3) * D * 8;
+      float v[VC][EPC];
 #pragma unroll
-      for (int dl = 0; dl < DL; ++dl) load8<T>(vp + dl * 8, v[dl]);
+      for (int i = 0; i < VC; ++i) load_col<T>(vt + (size_t)(64 * i + lane) * EPC, v[i]);
       if (p8 < ps || p8 + 8 > pe) {
         // edge group: slots outside [ps, pe) may hold anything (NaN): zero by select
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const bool ok = p8 + e >= ps && p8 + e < pe;
+        for (int e = 0; e < EPC; ++e) {
+          const bool ok = p8 + slot0 + e >= ps && p8 + slot0 + e < pe;
 #pragma unroll
-          for (int dl = 0; dl < DL; ++dl) v[dl][e] = ok ? v[dl][e] : 0.f;
+          for (int i = 0; i < VC; ++i) v[i][e] = ok ? v[i][e] : 0.f;
         }
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < EPC; ++e) {
         float pv[RB];
 #pragma unroll
-        for (int r = 0; r < RB; ++r) pv[r] = p_s[wave][8 * gi + e][r];
+        for (int r = 0; r < RB; ++r) pv[r] = p_s[wave][8 * gi + slot0 + e][r];
 #pragma unroll
         for (int r = 0; r < RB; ++r)
 #pragma unroll
-          for (int dl = 0; dl < DL; ++dl) acc[r][dl] = fmaf(pv[r], v[dl][e], acc[r][dl]);
+          for (int i = 0; i < VC; ++i) acc[r][i] = fmaf(pv[r], v[i][e], acc[r][i]);
       }
     }
     __builtin_amdgcn_wave_barrier();  // the weights are read before the next step writes them
   }
 
-  // exp-sums across lanes, then the waves' states in a fixed order
+  // exp-sums across lanes, the halves of each dim (fp32), then the waves'
+  // states in a fixed order
 #pragma unroll
   for (int r = 0; r < RB; ++r) lrun[r] = wave_sum(lrun[r]);
+  if constexpr (EPC < 8) {
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+      for (int i = 0; i < VC; ++i) acc[r][i] += __shfl_xor(acc[r][i], 1);
+  }
+  const bool writer = slot0 == 0;  // one lane per dim stores
   if (lane == 0) {
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
@@ -310,7 +352,7 @@ __device__ __forceinline__ void wave_run(const PartArgs& a, int b, int h, int L,
 #pragma unroll
     for (int r = 0; r < RB; ++r)
 #pragma unroll
-      for (int dl = 0; dl < DL; ++dl) o_s[wave - 1][r][lane * DL + dl] = acc[r][dl];
+      for (int i = 0; i < VC; ++i) o_s[wave - 1][r][vdim(i)] = acc[r][i];  // pairs: equal values
   }
   __syncthreads();
   if (wave != 0) return;  // (every wave returns; wave 0 after the stores below)
@@ -326,26 +368,28 @@ __device__ __forceinline__ void wave_run(const PartArgs& a, int b, int h, int L,
     const float mref = (M == -INFINITY) ? 0.f : M;
     const float f0 = __builtin_amdgcn_exp2f(m_s[0][r] - mref);
     float l = l_s[0][r] * f0;
-    float o[DL];
+    float o[VC];
 #pragma unroll
-    for (int dl = 0; dl < DL; ++dl) o[dl] = acc[r][dl] * f0;
+    for (int i = 0; i < VC; ++i) o[i] = acc[r][i] * f0;
 #pragma unroll
     for (int w = 1; w < NW; ++w) {
       const float fw = __builtin_amdgcn_exp2f(m_s[w][r] - mref);
       l += l_s[w][r] * fw;
 #pragma unroll
-      for (int dl = 0; dl < DL; ++dl) o[dl] += fw * o_s[w - 1][r][lane * DL + dl];
+      for (int i = 0; i < VC; ++i) o[i] += fw * o_s[w - 1][r][vdim(i)];
     }
     const float inv = l > 0.f ? 1.f / l : 0.f;
     if (one_shot) {
       const int i = n / G, g = n - i * G;
-      T* op = (T*)a.out + ((size_t)(qoff + i) * a.num_q_heads + (size_t)h * G + g) * D + lane * DL;
+      T* op = (T*)a.out + ((size_t)(qoff + i) * a.num_q_heads + (size_t)h * G + g) * D;
+      if (writer)
 #pragma unroll
-      for (int dl = 0; dl < DL; ++dl) store_elem<T>(op + dl, o[dl] * inv);
+        for (int c = 0; c < VC; ++c) store_elem<T>(op + vdim(c), o[c] * inv);
     } else {
-      float* op = a.ws_o + (wbase + n) * D + lane * DL;
+      float* op = a.ws_o + (wbase + n) * D;
+      if (writer)
 #pragma unroll
-      for (int dl = 0; dl < DL; ++dl) op[dl] = o[dl] * inv;
+        for (int c = 0; c < VC; ++c) op[vdim(c)] = o[c] * inv;
       if (lane == 0) {
         a.ws_m[wbase + n] = M;
         a.ws_l[wbase + n] = l;
