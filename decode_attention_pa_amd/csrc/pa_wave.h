@@ -55,9 +55,9 @@ __device__ inline float wave_sum(float x) {
 template <typename T>
 __device__ inline void load8(const T* p, float (&x)[8]);
 // Cached 16-byte loads, for K: a key instruction uses half of each line it
-// touches and the next one the other half, so the lines must stay cached
-// (measured on MI355X: non-temporal K loads made the fp32 GQA batch 36 %
-// slower).
+// touches and the next one the other half (measured on MI355X, fp32 GQA
+// batch: non-temporal K loads 2 % slower; with the earlier V mapping, whose
+// loads also leaned on the caches, 36 %).
 template <typename V>
 __device__ inline V ld16(const V* p) {
   return *p;
