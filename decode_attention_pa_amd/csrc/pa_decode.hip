@@ -326,15 +326,23 @@ pa_status make_plan(const pa_dims* d, int32_t window, int32_t hkv, int32_t bs, i
   const int w_req = o ? o->waves : 0;
   if (r.path == PA_PATH_MFMA && w_req == 0) {
     // Grid plans with few waves in flight, one-shot with under 16 waves per
-    // CU: rows in one-tile blocks of 4 waves (measured on MI355X: 512
-    // sliding-window MTP units of 32 rows, 10 % faster per call as 1024
-    // workgroups x 4 waves than as 512 x 2).
+    // CU: two row tiles run as one workgroup of 4 waves (each K/V load feeds
+    // both tiles, no second read through L2); more tiles go to one-tile
+    // blocks of 4 waves.  Measured on MI355X, 512 sliding-window MTP units
+    // of 32 rows: 1024 workgroups x 4 waves were 10 % faster per call than
+    // 512 x 2; 512 x 4 with both tiles ties with them (8.2-8.4 us per call
+    // warm, 12.4-12.8 flushed) and reads each K/V byte once instead of 1.18
+    // times.
     if (!r.persistent && r.one_shot && r.row_tiles > 1 && d->head_dim != 256 &&
         units * r.row_blocks * r.waves < 16 * (int64_t)num_cus) {
-      r.row_tiles = 1;
-      r.waves = 4;
-      r.block_rows = 16;
-      r.row_blocks = (r.rows + 15) / 16;
+      if (r.row_tiles == 2) {
+        r.waves = 4;
+      } else {
+        r.row_tiles = 1;
+        r.waves = 4;
+        r.block_rows = 16;
+        r.row_blocks = (r.rows + 15) / 16;
+      }
     }
     // Split plans at head dim 256 (~250 VGPRs, one or two waves per SIMD):
     // 2 waves per workgroup, so that twice as many workgroups share the CUs

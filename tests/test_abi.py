@@ -233,11 +233,11 @@ def test_streaming_loads_choice(lib):
     assert pa.plan(dims_of(long, num_blocks=10240), 0, 1, 16)["streaming"] == 1
     assert pa.plan(dims_of(long, num_blocks=10240), 0, 1, 16,
                    loads=pa.LOADS_CACHED)["streaming"] == 0
-    swa = workloads.WORKLOADS["swa_mtp_bf16"]         # one-shot, rows in two blocks
+    swa = workloads.WORKLOADS["swa_mtp_bf16"]         # one-shot, two tiles in one block
     p = pa.plan(dims_of(swa), 128, 8, 64)
-    assert (p["row_blocks"], p["streaming"]) == (2, 0)
-    p = pa.plan(dims_of(swa), 128, 8, 64, waves=2)    # two tiles, one block
     assert (p["row_blocks"], p["streaming"]) == (1, 1)
+    p = pa.plan(dims_of(swa, num_q_heads=96), 128, 8, 64)   # 48 rows: one-tile blocks
+    assert (p["row_blocks"], p["streaming"]) == (3, 0)
     pre = workloads.WORKLOADS["prefill_chunk_bf16"]   # 128 rows: four row blocks share K/V
     p = pa.plan(dims_of(pre), 0, 4, 16)
     assert p["row_blocks"] > 1 and p["streaming"] == 0
@@ -320,12 +320,15 @@ def test_binding_rejects_cpu_tensors():
 
 
 def test_grid_plans_with_few_waves(lib):
-    # One-shot grid plans under 16 waves per CU split their rows into
-    # one-tile blocks of 4 waves; with enough units, or waves forced, they
-    # keep all rows in one workgroup.
+    # One-shot grid plans under 16 waves per CU run two row tiles as one
+    # workgroup of 4 waves and more tiles as one-tile blocks of 4 waves; with
+    # enough units, or waves forced, all rows stay in one workgroup of the
+    # default waves.
     swa = workloads.WORKLOADS["swa_mtp_bf16"]        # 512 units x 32 rows, one-shot
     p = pa.plan(dims_of(swa), 128, 8, 64, num_cus=256)
-    assert (p["one_shot"], p["row_tiles"], p["row_blocks"], p["waves"]) == (1, 1, 2, 4)
+    assert (p["one_shot"], p["row_tiles"], p["row_blocks"], p["waves"]) == (1, 2, 1, 4)
+    p = pa.plan(dims_of(swa, num_q_heads=128), 128, 8, 64, num_cus=256)    # 64 rows
+    assert (p["one_shot"], p["row_tiles"], p["row_blocks"], p["waves"]) == (1, 1, 4, 4)
     big = dims_of(swa, batch=1024)                   # 8192 units: plenty of waves
     p = pa.plan(big, 128, 8, 64, num_cus=256)
     assert (p["row_tiles"], p["row_blocks"], p["waves"]) == (2, 1, 2)
