@@ -327,12 +327,12 @@ pa_status make_plan(const pa_dims* d, int32_t window, int32_t hkv, int32_t bs, i
   if (r.path == PA_PATH_MFMA && w_req == 0) {
     // Grid plans with few waves in flight, one-shot with under 16 waves per
     // CU: two row tiles run as one workgroup of 4 waves (each K/V load feeds
-    // both tiles, no second read through L2); more tiles go to one-tile
-    // blocks of 4 waves.  Measured on MI355X, 512 sliding-window MTP units
-    // of 32 rows: 1024 workgroups x 4 waves were 10 % faster per call than
-    // 512 x 2; 512 x 4 with both tiles ties with them (8.2-8.4 us per call
-    // warm, 12.4-12.8 flushed) and reads each K/V byte once instead of 1.18
-    // times.
+    // both tiles: half the load instructions and workgroups); more tiles go
+    // to one-tile blocks of 4 waves.  Measured on MI355X, 512 sliding-window
+    // MTP units of 32 rows: 1024 workgroups x 4 waves were 10 % faster per
+    // call than 512 x 2, and 512 x 4 with both tiles ties with them (8.2-8.4
+    // us per call warm, 12.4-12.8 flushed; the same HBM traffic, as the
+    // second block's reads hit L2).
     if (!r.persistent && r.one_shot && r.row_tiles > 1 && d->head_dim != 256 &&
         units * r.row_blocks * r.waves < 16 * (int64_t)num_cus) {
       if (r.row_tiles == 2) {
