@@ -48,6 +48,26 @@ struct GroupReduce {
       return op(op(op(lds[0][u], lds[1][u]), lds[2][u]), lds[3][u]);
     }
   }
+  // Sums of N values at once: one butterfly per value, one shared-memory
+  // round for all of them (waves added in wave order).
+  template <int N>
+  __device__ static void sum_n(float (&x)[N], float (*lds)[64][N]) {
+    if constexpr (GP > 1) {
+#pragma unroll
+      for (int off = UPW; off < 64; off <<= 1)
+#pragma unroll
+        for (int e = 0; e < N; ++e) x[e] += __shfl_xor(x[e], off);
+      const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+      __syncthreads();  // the previous use of lds is finished
+      if (lane < UPW)
+#pragma unroll
+        for (int e = 0; e < N; ++e) lds[wave][lane][e] = x[e];
+      __syncthreads();
+      const int u = lane % UPW;
+#pragma unroll
+      for (int e = 0; e < N; ++e) x[e] = ((lds[0][u][e] + lds[1][u][e]) + lds[2][u][e]) + lds[3][u][e];
+    }
+  }
 };
 
 // VEC = 4: a unit is 4 consecutive dims (head dims divisible by 4); VEC = 1:
@@ -60,6 +80,7 @@ __global__ __launch_bounds__(256) void lse_reduce(ReduceArgs a) {
   const int D = a.head_dim;
   const int D4 = D / VEC;                    // units per row
   __shared__ float lds[4][64];
+  __shared__ float lds_n[4][64][VEC + 1];
   const int h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   // One round of independent loads: lengths, run count, row offset.
@@ -126,10 +147,14 @@ __global__ __launch_bounds__(256) void lse_reduce(ReduceArgs a) {
   }
   const float M = GroupReduce<GP>::all(mt, lds, [](float x, float y) { return fmaxf(x, y); });
   const float r = (mt == -INFINITY) ? 0.f : exp2f(mt - M);
-  const auto add = [](float x, float y) { return x + y; };
+  float sums[VEC + 1];
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) acc[e] = GroupReduce<GP>::all(acc[e] * r, lds, add);
-  den = GroupReduce<GP>::all(den * r, lds, add);
+  for (int e = 0; e < VEC; ++e) sums[e] = acc[e] * r;
+  sums[VEC] = den * r;
+  GroupReduce<GP>::sum_n(sums, lds_n);
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = sums[e];
+  den = sums[VEC];
   if (gp != 0 || !live) return;
   const float inv = den > 0.f ? 1.f / den : 0.f;
   const int i = n / G, g = n - i * G;
