@@ -90,7 +90,17 @@ __host__ __device__ inline int k_slot_bytes(int slot, int row_bytes) {
 __device__ inline int wave_row_offset(const int32_t* __restrict__ query_lens, int b) {
   const int lane = threadIdx.x & 63;
   int s = 0;
-  for (int k = lane; k < b; k += 64) s += query_lens[k];
+  // the first 1024 sequences: every load requested before any is used (one
+  // round trip instead of one per 64 sequences)
+  int v[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    const int k = lane + 64 * c;
+    v[c] = k < b ? query_lens[k] : 0;
+  }
+#pragma unroll
+  for (int c = 0; c < 16; ++c) s += v[c];
+  for (int k = lane + 1024; k < b; k += 64) s += query_lens[k];
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
   return s;
