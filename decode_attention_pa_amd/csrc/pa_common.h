@@ -90,17 +90,19 @@ __host__ __device__ inline int k_slot_bytes(int slot, int row_bytes) {
 __device__ inline int wave_row_offset(const int32_t* __restrict__ query_lens, int b) {
   const int lane = threadIdx.x & 63;
   int s = 0;
-  // the first 1024 sequences: every load requested before any is used (one
-  // round trip instead of one per 64 sequences)
-  int v[16];
+  if (b <= 64) {  // (b is the same on every lane) one load per lane at most
+    if (lane < b) s = query_lens[lane];
+  } else {
+    // the first 1024 sequences: all of a lane's loads requested before any is
+    // used (one round trip instead of one per 64 sequences); lanes past b
+    // re-read the last entry, so no load needs a branch of its own
+    int v[16];
 #pragma unroll
-  for (int c = 0; c < 16; ++c) {
-    const int k = lane + 64 * c;
-    v[c] = k < b ? query_lens[k] : 0;
+    for (int c = 0; c < 16; ++c) v[c] = query_lens[min(lane + 64 * c, b - 1)];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) s += lane + 64 * c < b ? v[c] : 0;
+    for (int k = lane + 1024; k < b; k += 64) s += query_lens[k];
   }
-#pragma unroll
-  for (int c = 0; c < 16; ++c) s += v[c];
-  for (int k = lane + 1024; k < b; k += 64) s += query_lens[k];
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
   return s;

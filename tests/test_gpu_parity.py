@@ -119,21 +119,27 @@ def test_max_rows_and_edge_lengths():
                             BF16_TOL, f"edges D={D} w={win} path={path} sched={sched} P={P}")
 
 
-@pytest.mark.parametrize("B,sched", [(1024, pa.SCHED_PERSISTENT), (1100, pa.SCHED_AUTO),
-                                     (8192, pa.SCHED_AUTO), (65535, pa.SCHED_AUTO)])
+@pytest.mark.parametrize("B,sched", [(65, pa.SCHED_GRID), (130, pa.SCHED_AUTO),
+                                     (1024, pa.SCHED_GRID), (1024, pa.SCHED_PERSISTENT),
+                                     (1100, pa.SCHED_AUTO), (8192, pa.SCHED_AUTO),
+                                     (65535, pa.SCHED_AUTO)])
 def test_largest_batches(B, sched):
     """The persistent schedule's largest batch (1024 sequences, its prefix sums
     in shared memory) and larger ones, which the plan hands to the grid
     schedule with row offsets scanned once into the workspace.  Query
     lengths 0-3 make every row offset a long prefix sum; sampled sequences
-    include the last ones; 65535 is the largest batch the library takes."""
+    include the last ones; 65535 is the largest batch the library takes.
+    Up to 1024 sequences on the grid schedule, each workgroup sums its row
+    offset itself: one load per lane up to 64 sequences, all of a lane's
+    loads at once beyond (sequences 63-65 sampled)."""
     r = np.random.default_rng(B)
     qls = tuple(int(x) for x in r.integers(0, 4, size=B))
     lens = tuple(int(q + x) for q, x in zip(qls, r.integers(1, 400 if B <= 8192 else 120, size=B)))
     w = small(5, batch=B, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
               query_len=3, seq_lens=lens, query_lens=qls, max_seq_len=max(lens),
               max_blocks_per_seq=-(-max(lens) // 16) + 1)
-    pick = sorted(set(int(x) for x in r.choice(B, size=40, replace=False)) | {0, B - 2, B - 1})
+    pick = sorted(set(int(x) for x in r.choice(B, size=40, replace=False)) | {0, B - 2, B - 1}
+                  | {k for k in (63, 64, 65) if k < B})
     for win in (0, 33):
         c = workloads.make_case(w, device="cuda", window=win)
         say(f"[case] batch {B} window={win} schedule={sched}")
