@@ -600,7 +600,7 @@ __global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
   const int L = a.seq_lens[it.b];
   const int q = a.query_lens[it.b];
   const SeqView sv = seq_view(L, q, a.window, a.part_size);
-  if (it.j >= sv.nparts) return;  // empty partition: contributes nothing
+  if (it.j >= sv.nparts) return;  // past the unit's partitions: no state to store
   const int r0 = it.rb * 16 * NRT;                // first packed row of this block
   if (r0 >= a.group * q) return;                 // no row of this sequence is in it
   const int qoff = row_offset(a.qoffs, a.query_lens, it.b);

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void part_valu(PartArgs a) {
   const int L = a.seq_lens[b];
   const int q = a.query_lens[b];
   const SeqView sv = seq_view(L, q, a.window, a.part_size);
-  if (j >= sv.nparts) return;  // empty partition: contributes nothing
+  if (j >= sv.nparts) return;  // past the unit's partitions: no state to store
   const int G = a.group;
   const int rows_b = G * q;
   const int r0 = it.rb * RB;

@@ -405,7 +405,7 @@ __global__ __launch_bounds__(256) void part_wave(PartArgs a) {
   const int L = a.seq_lens[it.b];
   const int q = a.query_lens[it.b];
   const SeqView sv = seq_view(L, q, a.window, a.part_size);
-  if (it.j >= sv.nparts) return;         // empty partition: contributes nothing
+  if (it.j >= sv.nparts) return;         // past the unit's partitions: no state to store
   const int r0 = it.rb * RB;
   if (r0 >= a.group * q) return;         // no row of this sequence in this block
   const int qoff = __builtin_amdgcn_readfirstlane(row_offset(a.qoffs, a.query_lens, it.b));
