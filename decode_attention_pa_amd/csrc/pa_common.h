@@ -15,6 +15,58 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Cross-lane combines that stay in the vector ALUs (no trip through the LDS
+// crossbar, and no wait that also covers outstanding scalar loads, as a
+// ds_bpermute's would).  32-bit values (float or int); `op` must be
+// commutative: a lane may see its own value and its partner's in either
+// order, and both lanes of a pair get the same bits.  All lanes active.
+template <typename T>
+__device__ __forceinline__ uint32_t lane_bits(T x) {
+  return __builtin_bit_cast(uint32_t, x);
+}
+template <typename T>
+__device__ __forceinline__ T from_lane_bits(uint32_t x) {
+  return __builtin_bit_cast(T, x);
+}
+// op(x, x of lane ^ 16) and op(x, x of lane ^ 32): gfx950's row swaps
+// (v_permlane16_swap / v_permlane32_swap) of x with itself hand every lane
+// both values of its pair.
+template <typename T, typename F>
+__device__ __forceinline__ T xor16_op(T x, F op) {
+  const auto r = __builtin_amdgcn_permlane16_swap(lane_bits(x), lane_bits(x), false, false);
+  return op(from_lane_bits<T>(r[0]), from_lane_bits<T>(r[1]));
+}
+template <typename T, typename F>
+__device__ __forceinline__ T xor32_op(T x, F op) {
+  const auto r = __builtin_amdgcn_permlane32_swap(lane_bits(x), lane_bits(x), false, false);
+  return op(from_lane_bits<T>(r[0]), from_lane_bits<T>(r[1]));
+}
+// DPP controls: quad_perm [1,0,3,2] (lane ^ 1), [2,3,0,1] (lane ^ 2),
+// row_ror:8 (lane ^ 8 inside a 16-lane row), half-row and row mirrors.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppXor8 = 0x128;
+constexpr int kDppHalfMirror = 0x141, kDppMirror = 0x140;
+template <int CTRL, typename T>
+__device__ __forceinline__ T dpp(T x) {
+  return from_lane_bits<T>(__builtin_amdgcn_update_dpp(0, (int)lane_bits(x), CTRL, 0xF, 0xF, false));
+}
+// op over each 16-lane row, every lane receiving the result: lane ^ 1 and
+// lane ^ 2 leave every lane of a quad with the quad's value, the half-row
+// mirror meets each quad with the other quad of its half, the row mirror
+// each half with the other.  Associative, commutative ops (sums: one fixed
+// order, the same bits on every lane).
+template <typename T, typename F>
+__device__ __forceinline__ T row16_op(T x, F op) {
+  x = op(x, dpp<kDppXor1>(x));
+  x = op(x, dpp<kDppXor2>(x));
+  x = op(x, dpp<kDppHalfMirror>(x));
+  return op(x, dpp<kDppMirror>(x));
+}
+// op over the whole wave.
+template <typename T, typename F>
+__device__ __forceinline__ T wave_op(T x, F op) {
+  return row16_op(xor16_op(xor32_op(x, op), op), op);
+}
+
 // Positions per inner step of every partition kernel.  Partitions start on
 // multiples of this (relative to the aligned start of the span), so a chunk
 // never straddles two partitions.
@@ -103,9 +155,7 @@ __device__ inline int wave_row_offset(const int32_t* __restrict__ query_lens, in
     for (int c = 0; c < 16; ++c) s += lane + 64 * c < b ? v[c] : 0;
     for (int k = lane + 1024; k < b; k += 64) s += query_lens[k];
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-  return s;
+  return wave_op(s, [](int x, int y) { return x + y; });
 }
 
 // Batches above this size get their row offsets from a prefix array that a

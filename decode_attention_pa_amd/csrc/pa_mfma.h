@@ -212,13 +212,8 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
     const bool real = r0 + rt * 16 + ln < rows_b;
-    int lo_ = real ? tlo[rt] : INT32_MIN;
-    int hi_ = real ? thi[rt] : INT32_MAX;
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-      lo_ = max(lo_, __shfl_xor(lo_, off));
-      hi_ = min(hi_, __shfl_xor(hi_, off));
-    }
+    const int lo_ = row16_op(real ? tlo[rt] : INT32_MIN, [](int x, int y) { return max(x, y); });
+    const int hi_ = row16_op(real ? thi[rt] : INT32_MAX, [](int x, int y) { return min(x, y); });
     tlo_all[rt] = __builtin_amdgcn_readfirstlane(lo_);
     thi_all[rt] = __builtin_amdgcn_readfirstlane(hi_);
   }
@@ -400,8 +395,10 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
                                fmaxf(fmaxf(x[c][4], x[c][5]), fmaxf(x[c][6], x[c][7])));
         mx = c == 0 ? mc : fmaxf(mx, mc);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      {
+        const auto fmax = [](float x, float y) { return fmaxf(x, y); };
+        mx = xor32_op(xor16_op(mx, fmax), fmax);
+      }
       // Lazy rescaling: the reference max of a row moves only when the step
       // max exceeds it by more than kRescaleLog2 (or it is still -inf), so
       // weights stay <= 2^kRescaleLog2 and the accumulators are rescaled on
@@ -511,8 +508,8 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
     if constexpr (LSUM) {
       lrun[rt] = lacc[rt][0];
     } else {
-      lrun[rt] += __shfl_xor(lrun[rt], 16);
-      lrun[rt] += __shfl_xor(lrun[rt], 32);
+      const auto add = [](float x, float y) { return x + y; };
+      lrun[rt] = xor32_op(xor16_op(lrun[rt], add), add);
     }
   }
 

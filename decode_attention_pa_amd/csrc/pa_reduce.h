@@ -28,6 +28,16 @@ namespace pa {
 // a fixed xor butterfly inside each wave, then across the 4 waves through
 // shared memory in wave order: results are deterministic.
 // Grid: x = unit blocks of UPW units, y = KV head, z = sequence.
+// op of x with the lanes lane ^ U, lane ^ 2U, ... lane ^ 32 (U = 8, 16 or 32),
+// in that order.
+template <int U, typename F>
+__device__ __forceinline__ float xor_from(float x, F op) {
+  static_assert(U == 8 || U == 16 || U == 32, "lane strides 8, 16, 32");
+  if constexpr (U == 8) x = op(x, dpp<kDppXor8>(x));
+  if constexpr (U <= 16) x = xor16_op(x, op);
+  return xor32_op(x, op);
+}
+
 template <int GP>
 struct GroupReduce {
   static constexpr int UPW = 256 / GP;
@@ -38,8 +48,7 @@ struct GroupReduce {
     if constexpr (GP == 1) {
       return x;
     } else {
-#pragma unroll
-      for (int off = UPW; off < 64; off <<= 1) x = op(x, __shfl_xor(x, off));
+      x = xor_from<UPW>(x, op);
       const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
       __syncthreads();  // the previous use of lds is finished
       if (lane < UPW) lds[wave][lane] = x;
@@ -53,10 +62,9 @@ struct GroupReduce {
   template <int N>
   __device__ static void sum_n(float (&x)[N], float (*lds)[64][N]) {
     if constexpr (GP > 1) {
+      const auto add = [](float a, float b) { return a + b; };
 #pragma unroll
-      for (int off = UPW; off < 64; off <<= 1)
-#pragma unroll
-        for (int e = 0; e < N; ++e) x[e] += __shfl_xor(x[e], off);
+      for (int e = 0; e < N; ++e) x[e] = xor_from<UPW>(x[e], add);
       const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
       __syncthreads();  // the previous use of lds is finished
       if (lane < UPW)

@@ -40,15 +40,11 @@
 namespace pa {
 
 __device__ inline float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+  return wave_op(x, [](float a, float b) { return fmaxf(a, b); });
 }
 
 __device__ inline float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  return wave_op(x, [](float a, float b) { return a + b; });
 }
 
 // 8 consecutive elements at p as fp32 (16-byte loads).
@@ -338,7 +334,7 @@ __device__ __forceinline__ void wave_run(const PartArgs& a, int b, int h, int L,
 #pragma unroll
     for (int r = 0; r < RB; ++r)
 #pragma unroll
-      for (int i = 0; i < VC; ++i) acc[r][i] += __shfl_xor(acc[r][i], 1);
+      for (int i = 0; i < VC; ++i) acc[r][i] += dpp<kDppXor1>(acc[r][i]);
   }
   const bool writer = slot0 == 0;  // one lane per dim stores
   if (lane == 0) {
