@@ -137,25 +137,32 @@ __host__ __device__ inline int k_slot_bytes(int slot, int row_bytes) {
 }
 
 // Exclusive prefix sum of query_lens[0 .. b) computed by one wave; every lane
-// returns the sum.  Gives the first q/out row of sequence b in the packed
-// [sum q_b, H_q, D] layout.
-__device__ inline int wave_row_offset(const int32_t* __restrict__ query_lens, int b) {
+// gets the sum.  Gives the first q/out row of sequence b in the packed
+// [sum q_b, H_q, D] layout.  In two steps, so that a kernel can request the
+// first loads together with its other start-up loads: row_offset_issue
+// reads query_lens[lane] (lanes below b), row_offset_finish adds the rest.
+__device__ inline int row_offset_issue(const int32_t* __restrict__ query_lens, int b) {
   const int lane = threadIdx.x & 63;
-  int s = 0;
-  if (b <= 64) {  // (b is the same on every lane) one load per lane at most
-    if (lane < b) s = query_lens[lane];
-  } else {
-    // the first 1024 sequences: all of a lane's loads requested before any is
+  return lane < b ? query_lens[lane] : 0;
+}
+__device__ inline int wave_row_offset_finish(int first, const int32_t* __restrict__ query_lens, int b) {
+  const int lane = threadIdx.x & 63;
+  int s = first;
+  if (b > 64) {  // (b is the same on every lane)
+    // up to 1024 sequences: all of a lane's loads requested before any is
     // used (one round trip instead of one per 64 sequences); lanes past b
     // re-read the last entry, so no load needs a branch of its own
-    int v[16];
+    int v[15];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) v[c] = query_lens[min(lane + 64 * c, b - 1)];
+    for (int c = 1; c < 16; ++c) v[c - 1] = query_lens[min(lane + 64 * c, b - 1)];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) s += lane + 64 * c < b ? v[c] : 0;
+    for (int c = 1; c < 16; ++c) s += lane + 64 * c < b ? v[c - 1] : 0;
     for (int k = lane + 1024; k < b; k += 64) s += query_lens[k];
   }
   return wave_op(s, [](int x, int y) { return x + y; });
+}
+__device__ inline int wave_row_offset(const int32_t* __restrict__ query_lens, int b) {
+  return wave_row_offset_finish(row_offset_issue(query_lens, b), query_lens, b);
 }
 
 // Batches above this size get their row offsets from a prefix array that a
@@ -169,6 +176,12 @@ constexpr int kScanBatch = 1024;
 __device__ inline int row_offset(const int32_t* __restrict__ qoffs,
                                  const int32_t* __restrict__ query_lens, int b) {
   return qoffs ? qoffs[b] : wave_row_offset(query_lens, b);
+}
+// The same after row_offset_issue (whose loads are wasted when the scanned
+// array exists: batches above kScanBatch).
+__device__ inline int row_offset_finish(int first, const int32_t* __restrict__ qoffs,
+                                        const int32_t* __restrict__ query_lens, int b) {
+  return qoffs ? qoffs[b] : wave_row_offset_finish(first, query_lens, b);
 }
 
 __device__ inline float bf16_bits_to_f32(uint32_t bits16) {

@@ -594,13 +594,14 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
 template <int D, int NRT, int NW, bool STREAM, bool KV8, bool Q8>
 __global__ __launch_bounds__(64 * NW) void part_mfma(PartArgs a) {
   const PartItem it = part_item(a);
+  const int ro = row_offset_issue(a.query_lens, it.b);  // travels with the lengths
   const int L = a.seq_lens[it.b];
   const int q = a.query_lens[it.b];
   const SeqView sv = seq_view(L, q, a.window, a.part_size);
   if (it.j >= sv.nparts) return;  // past the unit's partitions: no state to store
   const int r0 = it.rb * 16 * NRT;                // first packed row of this block
   if (r0 >= a.group * q) return;                 // no row of this sequence is in it
-  const int qoff = row_offset(a.qoffs, a.query_lens, it.b);
+  const int qoff = row_offset_finish(ro, a.qoffs, a.query_lens, it.b);
   const size_t state = ((size_t)it.b * a.num_kv_heads + it.h) * a.num_parts + it.j;
   mfma_run<D, NRT, NW, STREAM, KV8, Q8, false>(a, it.b, it.h, L, q, qoff, sv, it.j, it.j, state,
                                                sv.nparts == 1, r0);

@@ -91,13 +91,20 @@ __global__ __launch_bounds__(256) void lse_reduce(ReduceArgs a) {
   __shared__ float lds_n[4][64][VEC + 1];
   const int h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
-  // One round of independent loads: lengths, run count, row offset.
+  // One round of independent loads: row offset, lengths, run count.
+  const int ro = row_offset_issue(a.query_lens, b);
   const int L = a.seq_lens[b];
   const int q = a.query_lens[b];
-  // persistent schedule: the unit's run count and first state slot
-  const int2 rs = a.ws_runs ? *(const int2*)(a.ws_runs + 2 * ((size_t)b * a.num_kv_heads + h))
-                            : make_int2(0, 0);
-  const int qoff = row_offset(a.qoffs, a.query_lens, b);  // all lanes still active
+  // persistent schedule: the unit's run count and first state slot.  Without
+  // it the pair is read from the partial maxima instead (this kernel runs
+  // only when they exist) and masked to zero: no branch, so the loads go out
+  // with the others.
+  const bool runs = a.ws_runs != nullptr;
+  const int32_t* rp = runs ? a.ws_runs + 2 * ((size_t)b * a.num_kv_heads + h)
+                           : (const int32_t*)a.ws_m;
+  const int keep = -(int)runs;  // all ones or zero
+  const int2 rs = make_int2(rp[0] & keep, rp[1] & keep);
+  const int qoff = row_offset_finish(ro, a.qoffs, a.query_lens, b);  // all lanes still active
   const int G = a.group;
   const SeqView sv = seq_view(L, q, a.window, a.part_size);
   // states to merge: one per partition, or the unit's run count

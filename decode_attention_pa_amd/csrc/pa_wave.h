@@ -398,13 +398,14 @@ __device__ __forceinline__ void wave_run(const PartArgs& a, int b, int h, int L,
 template <typename T, int D, int RB>
 __global__ __launch_bounds__(256) void part_wave(PartArgs a) {
   const PartItem it = part_item(a);
+  const int ro = row_offset_issue(a.query_lens, it.b);  // travels with the lengths
   const int L = a.seq_lens[it.b];
   const int q = a.query_lens[it.b];
   const SeqView sv = seq_view(L, q, a.window, a.part_size);
   if (it.j >= sv.nparts) return;         // past the unit's partitions: no state to store
   const int r0 = it.rb * RB;
   if (r0 >= a.group * q) return;         // no row of this sequence in this block
-  const int qoff = __builtin_amdgcn_readfirstlane(row_offset(a.qoffs, a.query_lens, it.b));
+  const int qoff = __builtin_amdgcn_readfirstlane(row_offset_finish(ro, a.qoffs, a.query_lens, it.b));
   const size_t state = ((size_t)it.b * a.num_kv_heads + it.h) * a.num_parts + it.j;
   wave_run<T, D, RB>(a, it.b, it.h, L, q, qoff, sv, it.j, it.j, state, sv.nparts == 1, r0);
 }
