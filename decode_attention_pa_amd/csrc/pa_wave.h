@@ -16,9 +16,10 @@
 //   mask  visible iff first_visible(row) <= pos <= row position, pos in the
 //         partition; masked scores become -inf by select.
 //   online softmax (log2 domain): each row's step max is a wave reduction
-//         (xor butterfly); the reference max moves only when a step beats it
-//         by more than 2^8 (as on the matrix cores); a row with nothing
-//         visible keeps -inf and never evaluates (-inf) - (-inf).
+//         (row swaps, then DPP inside 16-lane rows); the reference max
+//         moves only when a step beats it by more than 2^8 (as on the
+//         matrix cores); a row with nothing visible keeps -inf and never
+//         evaluates (-inf) - (-inf).
 //   PV    for each group of 8 positions the wave reads the group's [D][8] V
 //         tile as 16-byte columns, lane t taking columns t, t + 64, ... (each
 //         load instruction reads 1 KB contiguous, non-temporal): in bf16 a
