@@ -89,14 +89,18 @@ def test_small_f32(seed):
             compare(run_gpu(c, part_size=P), exp, rows, F32_TOL, f"small-f32 {seed} w={win} P={P}")
 
 
+@pytest.mark.parametrize("sched", [pa.SCHED_GRID, pa.SCHED_PERSISTENT], ids=["grid", "ps"])
 @pytest.mark.parametrize("waves", [1, 2, 4])
-def test_mfma_waves(waves):
+def test_mfma_waves(waves, sched):
+    """Every workgroup size on both schedules (the persistent one keeps the
+    lengths its prologue reads in shared memory with 2 or 4 waves and
+    reloads them with one)."""
     w = small(7, head_dim=128, num_q_heads=8, num_kv_heads=2, query_len=2)  # R = 8: one row tile
     c = workloads.make_case(w, device="cuda", window=0)
     exp, rows = oracle_out(c)
     for P in (32, 96, 256):
-        compare(run_gpu(c, path=pa.PATH_MFMA, waves=waves, part_size=P), exp, rows, BF16_TOL,
-                f"waves={waves} P={P}")
+        compare(run_gpu(c, path=pa.PATH_MFMA, waves=waves, part_size=P, schedule=sched), exp, rows,
+                BF16_TOL, f"waves={waves} sched={sched} P={P}")
 
 
 def test_max_rows_and_edge_lengths():
