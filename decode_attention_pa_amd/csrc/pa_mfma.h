@@ -45,6 +45,7 @@
 namespace pa {
 
 __device__ inline bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+__device__ inline u32x4 as_u32x4(bf16x8 x) { return __builtin_bit_cast(u32x4, x); }
 
 // 16-byte load of KV data.  STREAM = true marks it non-temporal (streamed past
 // the caches): on MI355X such loads sustain ~13 % more bandwidth on a
@@ -315,6 +316,23 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
     v_scale = *a.v_scale;
   }
   if constexpr (Q8) scale_log2 *= *a.q_scale;
+  // The logit scale folds into the exponent's argument: scores stay raw
+  // through the mask and the max (a positive factor commutes with both, in
+  // rounding too) and each weight is exp2(fma(s, scale, -m)), one vector
+  // instruction per score fewer.  A negative scale goes into the query's
+  // sign bits (exact); a zero one becomes the smallest normal, which leaves
+  // every weight at exactly 1 and keeps masked scores at -inf.
+  if (scale_log2 < 0.f) {
+    scale_log2 = -scale_log2;
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        if constexpr (Q8) qf[rt][s] ^= 0x8080808080808080ull;  // E4M3 sign bits
+        else qf[rt][s] = as_bf16x8(as_u32x4(qf[rt][s]) ^ 0x80008000u);
+      }
+  }
+  scale_log2 = fmaxf(scale_log2, 1.17549435e-38f);
 
   // Software pipeline, one step deep: the next step's K rows are requested
   // as soon as QK has consumed the current ones, its V columns as soon as PV
@@ -376,15 +394,15 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
           // every real row sees the whole chunk
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            x[c][e] = sa[e] * scale_log2;
-            x[c][4 + e] = sb[e] * scale_log2;
+            x[c][e] = sa[e];
+            x[c][4 + e] = sb[e];
           }
         } else {
           const int p8 = cs + 8 * lg;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            x[c][e] = (uint32_t)(p8 + e - tlo[rt]) <= span ? sa[e] * scale_log2 : -INFINITY;
-            x[c][4 + e] = (uint32_t)(p8 + 4 + e - tlo[rt]) <= span ? sb[e] * scale_log2 : -INFINITY;
+            x[c][e] = (uint32_t)(p8 + e - tlo[rt]) <= span ? sa[e] : -INFINITY;
+            x[c][4 + e] = (uint32_t)(p8 + 4 + e - tlo[rt]) <= span ? sb[e] : -INFINITY;
           }
         }
       }
@@ -397,7 +415,7 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
       }
       {
         const auto fmax = [](float x, float y) { return fmaxf(x, y); };
-        mx = xor32_op(xor16_op(mx, fmax), fmax);
+        mx = xor32_op(xor16_op(mx, fmax), fmax) * scale_log2;  // to the log2 domain
       }
       // Lazy rescaling: the reference max of a row moves only when the step
       // max exceeds it by more than kRescaleLog2 (or it is still -inf), so
@@ -421,7 +439,7 @@ __device__ __forceinline__ void mfma_run(const PartArgs& a, int b, int h, int L,
       for (int c = 0; c < CPS; ++c) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const __bf16 pe16 = (__bf16)__builtin_amdgcn_exp2f(x[c][e] - mref);
+          const __bf16 pe16 = (__bf16)__builtin_amdgcn_exp2f(fmaf(x[c][e], scale_log2, -mref));
           pb[c][rt][e] = pe16;
           // normalise by the weights PV actually applies
           if constexpr (!LSUM) psum += (float)pe16;

@@ -46,6 +46,19 @@ def test_fp8q_small(seed, sched):
                     f"fp8q small{100 + seed} sched={sched} w={win} P={P}")
 
 
+@pytest.mark.parametrize("scale", [-0.09, 0.0])
+def test_fp8q_negative_and_zero_scale(scale):
+    """A negative logit scale goes into the FP8 query codes' sign bits; a
+    zero one weighs every visible position the same."""
+    w = fp8q(small(105, scale=scale))
+    for win in (0, 5):
+        c = workloads.make_case(w, device="cuda", window=win)
+        say(f"[case] fp8q scale={scale} window={win}")
+        exp, rows = oracle_out(c)
+        for P in (0, 32):
+            compare(run_gpu(c, part_size=P), exp, rows, BF16_TOL, f"fp8q scale={scale} w={win} P={P}")
+
+
 @pytest.mark.parametrize("seed", range(2))
 def test_fp8q_head_dim_256(seed):
     w = fp8q(small(200 + seed, head_dim=256))

@@ -78,6 +78,22 @@ def test_small_bf16(seed, path, sched):
                     f"small{seed} path={path} sched={sched} w={win} P={P}")
 
 
+@pytest.mark.parametrize("path,sched", KERNELS[:3])
+@pytest.mark.parametrize("scale", [-0.11, 0.0, 2.5])
+def test_scale_sign_and_size(scale, path, sched):
+    """Scales the decode call may get besides 1/sqrt(D): negative (the
+    matrix-core kernels carry its sign in the query's sign bits), zero (every
+    visible position weighs the same) and large (sharp weights)."""
+    w = small(13, head_dim=128, num_q_heads=16, num_kv_heads=2, query_len=2, scale=scale)
+    for win in (0, 7):
+        c = workloads.make_case(w, device="cuda", window=win)
+        say(f"[case] scale={scale} path={path} schedule={sched} window={win}")
+        exp, rows = oracle_out(c)
+        for P in (0, 64):
+            compare(run_gpu(c, path=path, part_size=P, schedule=sched), exp, rows, BF16_TOL,
+                    f"scale={scale} path={path} sched={sched} w={win} P={P}")
+
+
 @pytest.mark.parametrize("seed", range(4))
 def test_small_f32(seed):
     w = small(seed + 40, dtype="f32")
