@@ -364,9 +364,14 @@ def test_grid_splits_sized_by_loads_in_flight(lib):
     assert plan(2, 64, 8, 64, 16384)["part_size"] == 512     # head dim 64: 2 workgroups per CU
     assert plan(1, 16, 2, 256, 16384)["part_size"] == 128    # head dim 256: 2 waves per CU
     assert plan(1, 8, 1, 128, 32768)["part_size"] == 256     # floor of 8 chunks
-    # two row tiles keep the ~8-workgroups-per-CU split
+    # two row tiles keep the ~8-workgroups-per-CU split (a longer partition
+    # for the states' sake would leave fewer than two workgroups per CU)
     r32 = plan(8, 32, 1, 128, 16384)
     assert (r32["row_tiles"], r32["part_size"]) == (2, 256)
+    # 128 rows per unit: partitions long enough that their states stay near
+    # 1/6 of the K/V they read (24 R (D + 2) / (D s) = 1560 -> 49 chunks)
+    r128 = plan(16, 32, 4, 128, 8192, q=16)
+    assert (r128["row_blocks"], r128["part_size"], r128["num_parts"]) == (4, 1568, 6)
 
 
 def test_fp8_query_format_rules(lib):
