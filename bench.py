@@ -67,8 +67,12 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(case) -> dict:
-    """Bytes the method must move for one call (see module docstring)."""
+def algorithmic_bytes(case, one_shot: bool = False) -> dict:
+    """Bytes the method must move for one call (see module docstring).
+    ``partition_kernel``: the share of them the partition kernel moves.  On a
+    one-shot plan it is the whole call (it writes the output rows itself);
+    on a split plan the merge writes them, and the partition kernel's own
+    writes are partial states, which the method does not need."""
     w = case.w
     s = 2 if w.dtype == "bf16" else 4
     skv = 1 if w.kv_dtype == "fp8" else s      # bytes per cached K / V element
@@ -87,7 +91,7 @@ def algorithmic_bytes(case) -> dict:
     lens = 8 * w.batch
     return dict(kv=kv, q=qb, out=ob, tables=tables, lens=lens,
                 total=kv + qb + ob + tables + lens,
-                partition_kernel=kv + qb + tables + lens)
+                partition_kernel=kv + qb + tables + lens + (ob if one_shot else 0))
 
 
 CALIB_COPIES = 3  # plain 1 GiB device copies issued by --copy-calibration
@@ -406,7 +410,7 @@ def side_lines(pa, workloads, main_case, a, flush_buf, reps) -> dict:
             call()
         torch.cuda.synchronize()
         per, kern = timed_reps(call, reps, flush_buf if flush else None)
-        nb = algorithmic_bytes(c_win)
+        nb = algorithmic_bytes(c_win, one_shot=bool(call.plan["one_shot"]))
         res[f"{name}:w{window}"] = {"flush_between_calls": flush, "plan": call.plan,
                                     "algorithmic_bytes": nb["total"], **summary(per, kern, nb),
                                     "read_ceiling": None}
@@ -493,7 +497,7 @@ def main(argv=None):
         torch.cuda.synchronize()
         del src, dst
 
-    nb = algorithmic_bytes(case)
+    nb = algorithmic_bytes(case, one_shot=bool(call.plan["one_shot"]))
     for _ in range(a.warmup):
         call()
     torch.cuda.synchronize()

@@ -91,6 +91,38 @@ __global__ __launch_bounds__(256) void lse_reduce(ReduceArgs a) {
   __shared__ float lds_n[4][64][VEC + 1];
   const int h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
+  const int unit = blockIdx.x * UPW + tid % UPW;
+  const int gp = tid / UPW;
+  const int n = unit / D4, d4 = unit % D4;
+  const bool runs = a.ws_runs != nullptr;
+
+  // States of one step: slots base + j0 + u*GP for u < U, those below
+  // `bound` and on a workspace row (n < rows); the rest stay neutral.
+  float mj[U], lj[U];
+  fvec o[U];
+  auto load_step = [&](size_t base, int j0, int bound) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int jj = j0 + u * GP;
+      mj[u] = -INFINITY;
+      lj[u] = 0.f;
+      o[u] = fvec{};
+      if (n < a.rows && jj < bound) {
+        const size_t w = (base + jj) * a.rows + n;
+        mj[u] = a.ws_m[w];
+        lj[u] = a.ws_l[w];
+        o[u] = *(const fvec*)(a.ws_o + w * D + d4 * VEC);
+      }
+    }
+  };
+  // Grid plan: partition j of unit (b, h) sits at slot (b * H_kv + h) * NP + j
+  // whatever the lengths, so the first step's states are requested with the
+  // lengths (one dependent round trip less) and masked once they arrive.
+  // Slots past this call's partitions hold stale contents, kept out by
+  // selects, never by multiplies.
+  const size_t grid_base = ((size_t)b * a.num_kv_heads + h) * a.num_parts;
+  if (!runs) load_step(grid_base, gp, a.num_parts);
+
   // One round of independent loads: row offset, lengths, run count.
   const int ro = row_offset_issue(a.query_lens, b);
   const int L = a.seq_lens[b];
@@ -99,7 +131,6 @@ __global__ __launch_bounds__(256) void lse_reduce(ReduceArgs a) {
   // it the pair is read from the partial maxima instead (this kernel runs
   // only when they exist) and masked to zero: no branch, so the loads go out
   // with the others.
-  const bool runs = a.ws_runs != nullptr;
   const int32_t* rp = runs ? a.ws_runs + 2 * ((size_t)b * a.num_kv_heads + h)
                            : (const int32_t*)a.ws_m;
   const int keep = -(int)runs;  // all ones or zero
@@ -108,44 +139,25 @@ __global__ __launch_bounds__(256) void lse_reduce(ReduceArgs a) {
   const int G = a.group;
   const SeqView sv = seq_view(L, q, a.window, a.part_size);
   // states to merge: one per partition, or the unit's run count
-  const int np = a.ws_runs ? rs.x : (sv.nparts > 1 ? min(sv.nparts, a.num_parts) : 0);
+  const int np = runs ? rs.x : (sv.nparts > 1 ? min(sv.nparts, a.num_parts) : 0);
   if (np <= 0) return;  // the partition kernel wrote these rows directly (whole workgroup)
-  const int unit = blockIdx.x * UPW + tid % UPW;
-  const int gp = tid / UPW;
-  const int n = unit / D4, d4 = unit % D4;
   // Lanes past the last row stay to the end: the combine below synchronises
   // the workgroup.  With GP = 1 there is no combine and they leave now.
   const bool live = n < G * q;
   if (GP == 1 && !live) return;
   // first state slot of the unit: partition j of a grid plan sits at slot
   // unit * NP + j; the persistent runs of a unit at consecutive slots
-  const size_t base = a.ws_runs ? (size_t)rs.y : ((size_t)b * a.num_kv_heads + h) * a.num_parts;
+  const size_t base = runs ? (size_t)rs.y : grid_base;
 
   // One pass: each thread keeps a running reference max mt over its own
   // partitions (rescaling its sums when it grows), then the group agrees on
   // M = max mt and every thread rescales by 2^(mt - M) before the sums.
+  // Every slot below np was written by this call's partition kernel, with
+  // finite values (a row that saw nothing stores m = -inf, l = 0, o = 0).
   float mt = -INFINITY;
   fvec acc = {};
   float den = 0.f;
-  for (int j0 = gp; j0 < np; j0 += GP * U) {
-    // Every slot below np was written by this call's partition kernel, with
-    // finite values (a row that saw nothing stores m = -inf, l = 0, o = 0),
-    // so all three are requested together: one round trip per step.
-    float mj[U], lj[U];
-    fvec o[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int jj = j0 + u * GP;
-      mj[u] = -INFINITY;
-      lj[u] = 0.f;
-      o[u] = fvec{};
-      if (live && jj < np) {
-        const size_t w = (base + jj) * a.rows + n;
-        mj[u] = a.ws_m[w];
-        lj[u] = a.ws_l[w];
-        o[u] = *(const fvec*)(a.ws_o + w * D + d4 * VEC);
-      }
-    }
+  auto fold = [&]() {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (mj[u] == -INFINITY) continue;  // partition where this row sees nothing
@@ -159,6 +171,23 @@ __global__ __launch_bounds__(256) void lse_reduce(ReduceArgs a) {
       acc += f * o[u];
       den += f;
     }
+  };
+  int j0 = gp;
+  if (!runs) {  // the speculative first step: keep this call's live slots
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool use = live && j0 + u * GP < np;
+      mj[u] = use ? mj[u] : -INFINITY;
+      lj[u] = use ? lj[u] : 0.f;
+      o[u] = use ? o[u] : fvec{};
+    }
+    fold();
+    j0 += GP * U;
+  }
+  for (; j0 < np; j0 += GP * U) {
+    // all three requested together: one round trip per step
+    load_step(base, j0, live ? np : 0);
+    fold();
   }
   const float M = GroupReduce<GP>::all(mt, lds, [](float x, float y) { return fmaxf(x, y); });
   const float r = (mt == -INFINITY) ? 0.f : exp2f(mt - M);

@@ -65,6 +65,9 @@ def test_algorithmic_bytes_match_a_position_count(case):
         assert got[k] == v, (k, got[k], v)
     assert got["partition_kernel"] == exp["kv"] + exp["q"] + exp["tables"] + exp["lens"]
     assert got["total"] == got["partition_kernel"] + exp["out"]
+    # a one-shot plan's partition kernel writes the output itself
+    whole = bench.algorithmic_bytes(case, one_shot=True)
+    assert whole["partition_kernel"] == whole["total"] == got["total"]
 
 
 def test_more_than_one_gpu_is_refused():
