@@ -337,9 +337,11 @@ REUSE_PLANS = [dict(part_size=32, schedule=pa.SCHED_GRID),      # 283 partitions
 
 
 def test_workspace_contents_do_not_matter():
-    """Every workspace byte a call reads was written by the same call: a
-    workspace full of random bytes, or left behind by calls with other plans,
-    gives the same output bits as a zeroed one."""
+    """Every workspace value that enters a call's arithmetic was written by
+    the same call (the merge requests a grid plan's first slots before it
+    knows how many a unit uses, and drops the stale ones by select): a
+    workspace full of random bytes, of NaN, or left behind by calls with
+    other plans, gives the same output bits as a zeroed one."""
     c = _case_for_reuse()
     dims = pa.dims_for(c.q, c.k_cache, c.block_tables, 2, c.w.max_seq_len)
     need = max(pa.workspace_size(dims, 0, 2, 32, **o) for o in REUSE_PLANS)
@@ -352,7 +354,10 @@ def test_workspace_contents_do_not_matter():
     for rep in range(2):
         for o, expect in zip(REUSE_PLANS, ref_out):
             assert torch.equal(run_gpu(c, workspace=ws, **o), expect), (rep, o)
-    say("[workspace] random and reused workspaces: identical outputs")
+    ws.fill_(255)  # every fp32 word 0xffffffff: a NaN
+    for o, expect in zip(REUSE_PLANS, ref_out):
+        assert torch.equal(run_gpu(c, workspace=ws, **o), expect), ("nan", o)
+    say("[workspace] random, NaN and reused workspaces: identical outputs")
 
 
 def test_graph_replays_match_eager():
