@@ -59,7 +59,7 @@ def random_case(seed):
     return w, win, opts
 
 
-@pytest.mark.parametrize("seed", range(48))
+@pytest.mark.parametrize("seed", range(400))
 def test_random_shape(seed):
     w, win, opts = random_case(7000 + seed)
     dims = pa.make_dims(w.batch, w.num_q_heads, w.head_dim, w.query_len, w.max_seq_len,
