@@ -396,30 +396,47 @@ SIDE = (("gqa_bf16", 0, True), ("long_splitk_bf16", 0, True), ("swa_mtp_bf16", 1
         ("large_block_mtp_bf16", 4096, False), ("gqa_f32", 0, True))
 
 
+def side_line(pa, workloads, main_case, a, flush_buf, reps, name, window, flush) -> dict:
+    import torch
+    if name == main_case.w.name:
+        c = main_case             # another window over the same cache
+    else:
+        c = workloads.make_case(workloads.WORKLOADS[name], device="cuda", window=window)
+    c_win = workloads.Case(**{**c.__dict__, "window": window})
+    call = make_call(pa, c_win, window, a)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    per, kern = timed_reps(call, reps, flush_buf if flush else None)
+    nb = algorithmic_bytes(c_win, one_shot=bool(call.plan["one_shot"]))
+    line = {"flush_between_calls": flush, "plan": call.plan, "algorithmic_bytes": nb["total"],
+            **summary(per, kern, nb), "read_ceiling": None}
+    rc = read_ceiling(pa, nb["partition_kernel"], flush_buf if flush else None)
+    achieved = nb["partition_kernel"] / (line["kernel_us"]["median"] * 1e-6) / 1e9
+    line["read_ceiling"] = with_share(rc, achieved)
+    return line
+
+
+def guarded(label, fn):
+    """fn() for one of the figures reported beside the headline; an exception
+    is printed to stderr and recorded in the line instead of losing the
+    headline measured before it."""
+    import traceback
+    try:
+        return fn()
+    except Exception as e:  # reported, never silently dropped
+        traceback.print_exc()
+        print(f"bench: {label} failed: {e!r}", file=sys.stderr, flush=True)
+        return {"error": f"{type(e).__name__}: {e}"}
+
+
 def side_lines(pa, workloads, main_case, a, flush_buf, reps) -> dict:
     import torch
     res = {}
     for name, window, flush in SIDE:
-        if name == main_case.w.name:
-            c = main_case             # another window over the same cache
-        else:
-            c = workloads.make_case(workloads.WORKLOADS[name], device="cuda", window=window)
-        c_win = workloads.Case(**{**c.__dict__, "window": window})
-        call = make_call(pa, c_win, window, a)
-        for _ in range(3):
-            call()
-        torch.cuda.synchronize()
-        per, kern = timed_reps(call, reps, flush_buf if flush else None)
-        nb = algorithmic_bytes(c_win, one_shot=bool(call.plan["one_shot"]))
-        res[f"{name}:w{window}"] = {"flush_between_calls": flush, "plan": call.plan,
-                                    "algorithmic_bytes": nb["total"], **summary(per, kern, nb),
-                                    "read_ceiling": None}
-        rc = read_ceiling(pa, nb["partition_kernel"], flush_buf if flush else None)
-        achieved = nb["partition_kernel"] / (res[f"{name}:w{window}"]["kernel_us"]["median"] * 1e-6) / 1e9
-        res[f"{name}:w{window}"]["read_ceiling"] = with_share(rc, achieved)
-        del call, c_win
-        if c is not main_case:
-            del c
+        res[f"{name}:w{window}"] = guarded(
+            f"side line {name} w={window}",
+            lambda: side_line(pa, workloads, main_case, a, flush_buf, reps, name, window, flush))
         torch.cuda.empty_cache()
     return res
 
@@ -580,7 +597,7 @@ def main(argv=None):
         "read_ceiling": with_share(read_ceiling(pa, nb["partition_kernel"], own_flush), achieved),
     }
     if not a.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(case, out, a.cpu_budget)
+        res["cpu_baseline"] = guarded("cpu_baseline", lambda: cpu_baseline(case, out, a.cpu_budget))
     if not a.no_side:
         del call
         res["side"] = side_lines(pa, workloads, case, a, flush_buf, a.reps)

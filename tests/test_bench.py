@@ -120,3 +120,12 @@ def test_parity_sample_keeps_extremes():
             assert int(np.argmax(lens)) in s and int(np.argmin(lens)) in s
             assert len(s) >= min(n, len(lens)) and s == sorted(set(s))
     assert sample_sequences([5, 6, 7], None, 0) == [0, 1, 2]
+
+
+def test_side_figures_that_fail_are_recorded_not_lost(capsys):
+    # a failing figure beside the headline is reported in the line and on
+    # stderr; a working one passes through unchanged
+    got = bench.guarded("side line x", lambda: 1 // 0)
+    assert got == {"error": "ZeroDivisionError: integer division or modulo by zero"}
+    assert "side line x failed" in capsys.readouterr().err
+    assert bench.guarded("y", lambda: {"value": 1}) == {"value": 1}
