@@ -474,3 +474,85 @@ def test_binding_rejects_tensors_and_streams_of_another_device():
         pa._stream_handle(FakeStream(), torch.device("cuda", 0))
     assert e.value.status == pa.ERR_INVALID_ARG
     assert pa._stream_handle(FakeStream(), torch.device("cuda", 1)).value is None
+
+
+def _align256(n):
+    return (n + 255) // 256 * 256
+
+
+# (row tiles, waves) instantiated for the matrix-core kernels at head dims 64 / 128
+MFMA_SHAPES = {(1, 1), (1, 2), (1, 4), (2, 1), (2, 2), (2, 4), (3, 1), (4, 1)}
+
+
+def test_plan_invariants_on_random_shapes(lib):
+    """What the kernels take for granted about a plan, over seeded random
+    shapes, windows, CU counts and forced options: partitions cover the
+    windowed span on the 32-position grid, row blocks cover the rows, only
+    instantiated (row tiles, waves) pairs, the persistent schedule only where
+    it exists, and the workspace bytes the header documents."""
+    import numpy as np
+    r = np.random.default_rng(2024)
+    planned = refused = 0
+    for _ in range(4000):
+        dtype = pa.F32 if r.random() < 0.2 else pa.BF16
+        kv = pa.KV_FP8_E4M3 if dtype == pa.BF16 and r.random() < 0.25 else pa.KV_NATIVE
+        qf = pa.Q_FP8_E4M3 if kv == pa.KV_FP8_E4M3 and r.random() < 0.4 else pa.Q_NATIVE
+        D = int(r.choice([64, 128, 256, 40, 66, 96, 200]))
+        hkv = int(r.choice([1, 2, 4, 8]))
+        G = int(r.choice([1, 2, 4, 5, 8, 16]))
+        ql = int(r.choice([1, 2, 4, 16, 64, 128]))
+        bs = int(r.choice([16, 32, 64, 256, 1024]))
+        B = int(r.choice([0, 1, 3, 32, 128, 1100, 5000]))
+        L = int(r.choice([ql, 100, 4096, 65536, 131072]))
+        L = max(L, ql)
+        win = int(r.choice([0, 0, 1, 7, 128, 4096, 100000]))
+        cus = int(r.choice([256, 80, 304, 1]))
+        opts = {}
+        if r.random() < 0.3:
+            opts["part_size"] = int(r.choice([32, 64, 192, 1024, 4096]))
+        if r.random() < 0.2:
+            opts["schedule"] = int(r.choice([pa.SCHED_GRID, pa.SCHED_PERSISTENT]))
+        if r.random() < 0.15:
+            opts["waves"] = int(r.choice([1, 2, 4]))
+        dims = pa.make_dims(B, G * hkv, D, ql, L, -(-L // bs), 1000, dtype, kv, qf)
+        try:
+            p = pa.plan(dims, win, hkv, bs, num_cus=cus, **opts)
+        except pa.PaError as e:
+            assert e.status in (pa.ERR_UNSUPPORTED, pa.ERR_INVALID_ARG), e
+            refused += 1
+            continue
+        planned += 1
+        R = G * ql
+        span = min(L, win + ql - 1) if win else L
+        assert p["rows"] == R and p["span_max"] == span, p
+        P = p["part_size"]
+        assert P >= 32 and P % 32 == 0, p
+        assert p["num_parts"] == -(-(span + 31) // P) or (p["num_parts"] == 1 and P >= span + 31), p
+        assert p["one_shot"] == (p["num_parts"] == 1), p
+        assert p["row_blocks"] * p["block_rows"] >= R > (p["row_blocks"] - 1) * p["block_rows"], p
+        assert p["waves"] in (1, 2, 4), p
+        if kv == pa.KV_FP8_E4M3:
+            assert p["path"] == pa.PATH_MFMA, p
+        if dtype == pa.F32:
+            assert p["path"] != pa.PATH_MFMA, p
+        if p["path"] == pa.PATH_MFMA:
+            assert D in (64, 128, 256) and p["block_rows"] == 16 * p["row_tiles"], p
+            pair = (p["row_tiles"], p["waves"])
+            assert pair in (MFMA_SHAPES if D != 256 else {(1, 1), (1, 2), (1, 4)}), p
+        else:
+            assert p["streaming"] == 0, p
+        if p["persistent"]:
+            assert p["path"] in (pa.PATH_MFMA, pa.PATH_VALU) and B <= 1024, p
+            assert p["row_blocks"] == 1 and p["ps_grid"] > 0, p
+        else:
+            assert p["ps_grid"] == 0, p
+        # workspace: 256-byte aligned regions of maxima, exp-sums, outputs,
+        # run records (persistent) and row offsets (batches above 1024)
+        units = B * hkv
+        slots = 0 if p["one_shot"] else (p["ps_grid"] + units if p["persistent"] else units * p["num_parts"])
+        S = slots * R
+        ws = 2 * _align256(S * 4) + _align256(S * D * 4)
+        ws += _align256(units * 8) if p["persistent"] and not p["one_shot"] else 0
+        ws += _align256(B * 4) if B > 1024 else 0
+        assert p["workspace_bytes"] == ws, (p, ws)
+    assert planned > 2000 and refused > 0, (planned, refused)
